@@ -1,0 +1,181 @@
+"""Pins for the CPU oracle: checks that tie it to facts outside itself.
+
+Each ``check_*`` takes an implementation and raises AssertionError when the
+implementation disagrees with a closed form, a hand-worked example, a library
+routine or an invariant of causal linear attention.  The tests run them on the
+oracle (must pass) and on deliberately wrong variants (must fail), so every pin
+is shown to catch at least one plausible mistake.
+
+Implementation signatures:
+    fwd(q, k, v) -> o                    q, k, v: [n, d] float arrays
+    blk(q, k, v, B) -> o                 block form with block size B
+    dec(q, k, v, S0) -> (o, S_final)     q, k, v: [steps, units, d], S0 [units, d, d]
+    varlen(q, k, v, cu) -> o             q, k, v: [heads, T, d]
+"""
+import json
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _arr(x):
+    return np.asarray(x, dtype=np.float32)
+
+
+def check_golden_causal(fwd):
+    g = load_golden("hand_causal_d2_n3.json")
+    o = fwd(_arr(g["q"]), _arr(g["k"]), _arr(g["v"]))
+    assert np.array_equal(np.asarray(o, np.float64), np.asarray(g["o"], np.float64)), o
+
+
+def check_golden_ones(fwd):
+    g = load_golden("hand_ones_d4_n5.json")
+    o = fwd(_arr(g["q"]), _arr(g["k"]), _arr(g["v"]))
+    assert np.array_equal(np.asarray(o, np.float64), np.asarray(g["o"], np.float64)), o
+
+
+def check_golden_block(blk):
+    g = load_golden("hand_block_d1_n4.json")
+    o = blk(_arr(g["q"]), _arr(g["k"]), _arr(g["v"]), g["block_size"])
+    assert np.array_equal(np.asarray(o, np.float64), np.asarray(g["o"], np.float64)), o
+
+
+def check_golden_decode(dec):
+    g = load_golden("hand_causal_d2_n3.json")
+    q = _arr(g["q"])[:, None, :]
+    k = _arr(g["k"])[:, None, :]
+    v = _arr(g["v"])[:, None, :]
+    states = []
+    S = np.zeros((1, 2, 2))
+    outs = []
+    for t in range(3):
+        o, S = dec(q[t:t + 1], k[t:t + 1], v[t:t + 1], S)
+        outs.append(np.asarray(o)[0, 0])
+        states.append(np.asarray(S)[0])
+    assert np.array_equal(np.array(outs), np.asarray(g["decode_o"], np.float64)), outs
+    assert np.array_equal(np.array(states), np.asarray(g["decode_states"], np.float64)), states
+
+
+def check_all_ones(fwd, n=37, d=8):
+    """Closed form: all-ones inputs give o_i = d (i + 1) in every component."""
+    one = np.ones((n, d), np.float32)
+    o = np.asarray(fwd(one, one, one))
+    expect = (d * (np.arange(n) + 1.0))[:, None] * np.ones((1, d))
+    assert np.array_equal(o, expect)
+
+
+def check_one_hot(fwd, n=70, d=6, j0s=(0, 15, 16, 31, 63, 64, 69), a=2, c=4):
+    """Closed form: k_{j0} = e_a, v_{j0} = e_c, all other k, v zero, every q_i = e_a:
+    o_i = [i >= j0] e_c."""
+    for j0 in j0s:
+        q = np.zeros((n, d), np.float32)
+        q[:, a] = 1
+        k = np.zeros((n, d), np.float32)
+        v = np.zeros((n, d), np.float32)
+        k[j0, a] = 1
+        v[j0, c] = 1
+        o = np.asarray(fwd(q, k, v))
+        expect = np.zeros((n, d))
+        expect[j0:, c] = 1
+        assert np.array_equal(o, expect), j0
+
+
+def check_prefix_sum(fwd, n=300, d=4, seed=7):
+    """q_i = k_j = e_0 and v_j = x_j e_0 turn o_i[0] into the inclusive cumulative
+    sum of x (compared with numpy.cumsum on small integers, so exactly)."""
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-5, 6, size=n).astype(np.float32)
+    q = np.zeros((n, d), np.float32)
+    q[:, 0] = 1
+    k = q.copy()
+    v = np.zeros((n, d), np.float32)
+    v[:, 0] = x
+    o = np.asarray(fwd(q, k, v))
+    assert np.array_equal(o[:, 0], np.cumsum(x.astype(np.float64)))
+    assert np.all(o[:, 1:] == 0)
+
+
+def check_vs_numpy_masked(fwd, n=50, d=7, seed=3, tol=1e-12):
+    """Textbook matrix form tril(Q K^T) V (numpy) on random inputs."""
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((n, d)).astype(np.float32) for _ in range(3))
+    ref = np.tril(q.astype(np.float64) @ k.astype(np.float64).T) @ v.astype(np.float64)
+    o = np.asarray(fwd(q, k, v))
+    assert np.max(np.abs(o - ref)) <= tol * np.max(np.abs(ref))
+
+
+def check_block_invariance(blk, fwd, n=133, d=5, Bs=(1, 2, 7, 16, 64, 133, 500), seed=11,
+                           tol=1e-12):
+    """The intra/inter split computes the same result for every block size."""
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((n, d)).astype(np.float32) for _ in range(3))
+    ref = np.asarray(fwd(q, k, v))
+    for B in Bs:
+        o = np.asarray(blk(q, k, v, B))
+        assert np.max(np.abs(o - ref)) <= tol * np.max(np.abs(ref)), B
+
+
+def check_integer_exact(fwd, ref_fn, n=40, d=6, seed=5):
+    """Small-integer inputs: every partial sum is an exact integer in double, so
+    the implementation must agree bit for bit with an exact reference."""
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.integers(-2, 3, size=(n, d)).astype(np.float32) for _ in range(3))
+    o = np.asarray(fwd(q, k, v), np.float64)
+    ref = np.asarray(ref_fn(q, k, v), np.float64)
+    assert np.array_equal(o, ref)
+
+
+def check_varlen_resets(varlen, fwd, lengths=(5, 0, 17, 1, 64, 33), heads=3, d=4, seed=9):
+    """Each packed sequence starts from an empty state: the packed result equals
+    running every sequence alone."""
+    rng = np.random.default_rng(seed)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    q, k, v = (rng.standard_normal((heads, T, d)).astype(np.float32) for _ in range(3))
+    o = np.asarray(varlen(q, k, v, cu))
+    for h in range(heads):
+        for s in range(len(lengths)):
+            a, b = cu[s], cu[s + 1]
+            if b > a:
+                ref = np.asarray(fwd(q[h, a:b], k[h, a:b], v[h, a:b]))
+                assert np.allclose(o[h, a:b], ref, rtol=0, atol=1e-12 * max(1.0, np.abs(ref).max())), (h, s)
+
+
+def check_decode_state_sum(dec, steps=20, units=3, d=5, seed=13):
+    """S_T = S_0 + sum_t k_t^T v_t, i.e. S_0 + K^T V as one matrix product."""
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((steps, units, d)).astype(np.float32) for _ in range(3))
+    S0 = rng.standard_normal((units, d, d))
+    _, S = dec(q, k, v, S0)
+    for u in range(units):
+        K = k[:, u, :].astype(np.float64)
+        V = v[:, u, :].astype(np.float64)
+        assert np.allclose(S[u], S0[u] + K.T @ V, rtol=0, atol=1e-12 * np.abs(S0[u] + K.T @ V).max())
+
+
+def check_decode_vs_prefill(dec, fwd, steps=25, d=6, seed=17):
+    """From an empty state the decode output (state before the token) plus the
+    token's own term (q.k) v equals the causal (j <= i) prefill output."""
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((steps, 1, d)).astype(np.float32) for _ in range(3))
+    o_dec, _ = dec(q, k, v, np.zeros((1, d, d)))
+    o_pre = np.asarray(fwd(q[:, 0], k[:, 0], v[:, 0]))
+    own = np.sum(q[:, 0].astype(np.float64) * k[:, 0], axis=1)[:, None] * v[:, 0]
+    lhs = np.asarray(o_dec)[:, 0] + own
+    assert np.max(np.abs(lhs - o_pre)) <= 1e-12 * np.abs(o_pre).max()
+
+
+def check_linearity(fwd, n=30, d=5, seed=19):
+    """o is linear in q and in v: o(2q) = 2 o(q); o(v1 + v2) = o(v1) + o(v2)."""
+    rng = np.random.default_rng(seed)
+    q, k, v1, v2 = (rng.integers(-3, 4, size=(n, d)).astype(np.float32) for _ in range(4))
+    o = np.asarray(fwd(q, k, v1))
+    assert np.array_equal(np.asarray(fwd(2 * q, k, v1)), 2 * o)
+    assert np.array_equal(np.asarray(fwd(q, k, v1 + v2)), o + np.asarray(fwd(q, k, v2)))

@@ -1,0 +1,219 @@
+"""The CPU oracle against hand-worked examples, closed forms, library routines and
+invariants (no GPU).  Mutant implementations show each pin catches a plausible
+mistake."""
+import numpy as np
+import pytest
+
+import pins
+
+
+@pytest.fixture(scope="module")
+def O(oracle_mod):
+    return oracle_mod
+
+
+def forms(O):
+    return {
+        "naive": lambda q, k, v: O.causal_linear_attention(q, k, v, "naive"),
+        "recurrent": lambda q, k, v: O.causal_linear_attention(q, k, v, "recurrent"),
+        "block64": lambda q, k, v: O.causal_linear_attention(q, k, v, "block", 64),
+        "block3": lambda q, k, v: O.causal_linear_attention(q, k, v, "block", 3),
+    }
+
+
+def blk(O):
+    return lambda q, k, v, B: O.causal_linear_attention(q, k, v, "block", B)
+
+
+def dec(O):
+    return lambda q, k, v, S0: O.decode(q, k, v, S0)
+
+
+def varlen(O, form="recurrent"):
+    return lambda q, k, v, cu: O.causal_linear_attention_varlen(q, k, v, cu, form, 16)
+
+
+# ---------------------------------------------------------------- oracle passes
+
+@pytest.mark.parametrize("name", ["naive", "recurrent", "block64", "block3"])
+def test_forms_pass_closed_forms(O, name):
+    f = forms(O)[name]
+    pins.check_golden_causal(f)
+    pins.check_golden_ones(f)
+    pins.check_all_ones(f)
+    pins.check_one_hot(f)
+    pins.check_prefix_sum(f)
+    pins.check_vs_numpy_masked(f)
+    pins.check_linearity(f)
+
+
+def test_block_form_golden_and_invariance(O):
+    pins.check_golden_block(blk(O))
+    pins.check_block_invariance(blk(O), forms(O)["naive"])
+
+
+def test_block_form_special_cases(O):
+    """B >= n is the masked matrix form; B = 1 is the token recurrence."""
+    rng = np.random.default_rng(23)
+    q, k, v = (rng.standard_normal((41, 9)).astype(np.float32) for _ in range(3))
+    full = O.causal_linear_attention(q, k, v, "block", 41)
+    assert np.allclose(full, O.numpy_masked(q, k, v), rtol=0, atol=1e-12 * np.abs(full).max())
+    one = O.causal_linear_attention(q, k, v, "block", 1)
+    rec = O.causal_linear_attention(q, k, v, "recurrent")
+    assert np.allclose(one, rec, rtol=0, atol=1e-12 * np.abs(rec).max())
+
+
+def test_naive_equals_recurrent_random(O):
+    """Associativity: sum_j (q.k_j) v_j == q (sum_j k_j^T v_j), in fp64."""
+    rng = np.random.default_rng(29)
+    q, k, v = (rng.standard_normal((3, 257, 64)).astype(np.float32) for _ in range(3))
+    a = O.causal_linear_attention(q, k, v, "naive")
+    b = O.causal_linear_attention(q, k, v, "recurrent")
+    assert O.rel_err(a, b) < 1e-12
+
+
+def test_integer_exact_against_fractions(O):
+    exact = lambda q, k, v: np.array(O.fraction_bruteforce(q, k, v), dtype=np.float64)
+    for f in forms(O).values():
+        pins.check_integer_exact(f, exact)
+
+
+def test_fraction_bruteforce_random_dyadic(O):
+    """Dyadic inputs (few mantissa bits): fp64 sums are exact, so the oracle must
+    equal exact rational arithmetic."""
+    rng = np.random.default_rng(31)
+    q, k, v = (np.round(rng.standard_normal((12, 5)) * 8) / 8 for _ in range(3))
+    exact = np.array(O.fraction_bruteforce(q, k, v), dtype=np.float64)
+    for name in ("naive", "recurrent", "block3"):
+        assert np.array_equal(forms(O)[name](q.astype(np.float32), k.astype(np.float32),
+                                             v.astype(np.float32)), exact), name
+
+
+def test_varlen(O):
+    pins.check_varlen_resets(varlen(O), forms(O)["naive"])
+    pins.check_varlen_resets(varlen(O, "naive"), forms(O)["recurrent"])
+    pins.check_varlen_resets(varlen(O, "block"), forms(O)["naive"])
+
+
+def test_decode(O):
+    pins.check_golden_decode(dec(O))
+    pins.check_decode_state_sum(dec(O))
+    pins.check_decode_vs_prefill(dec(O), forms(O)["naive"])
+
+
+def test_recurrent_rows_and_final_state(O):
+    rng = np.random.default_rng(37)
+    q, k, v = (rng.standard_normal((300, 16)).astype(np.float32) for _ in range(3))
+    full = O.causal_linear_attention(q, k, v, "recurrent")
+    rows = np.array([0, 1, 63, 64, 255, 299])
+    assert np.array_equal(O.recurrent_rows(q, k, v, rows), full[rows])
+    o, S = O.recurrent_final_state(q, k, v)
+    assert np.allclose(S, k.astype(np.float64).T @ v, rtol=0, atol=1e-12 * np.abs(S).max())
+    # Resuming from the final state of the first half gives the second half.
+    o1, S1 = O.recurrent_final_state(q[:100], k[:100], v[:100])
+    o2, _ = O.recurrent_final_state(q[100:], k[100:], v[100:], S1)
+    assert O.rel_err(np.concatenate([o1, o2]), full) < 1e-13
+
+
+def test_empty_inputs(O):
+    z = np.zeros((0, 8), np.float32)
+    assert O.causal_linear_attention(z, z, z).shape == (0, 8)
+    z3 = np.zeros((2, 0, 8), np.float32)
+    assert O.causal_linear_attention_varlen(z3, z3, z3, np.array([0, 0, 0])).shape == (2, 0, 8)
+
+
+def test_rel_err_metric(O):
+    assert O.rel_err([1.0, -4.0], [1.0, -4.0]) == 0.0
+    assert O.rel_err([1.5, -4.0], [1.0, -4.0]) == pytest.approx(0.125)
+
+
+# ------------------------------------------------- mutants: the pins must bite
+
+def _np_causal(q, k, v, strict=False, transpose_state=False):
+    q = q.astype(np.float64); k = k.astype(np.float64); v = v.astype(np.float64)
+    n, d = q.shape
+    out = np.zeros((n, d))
+    S = np.zeros((d, d))
+    for t in range(n):
+        if not strict:
+            S += np.outer(k[t], v[t])
+        out[t] = q[t] @ (S.T if transpose_state else S)
+        if strict:
+            S += np.outer(k[t], v[t])
+    return out
+
+
+def _np_block_no_inter(q, k, v, B):
+    q = q.astype(np.float64); k = k.astype(np.float64); v = v.astype(np.float64)
+    n, _ = q.shape
+    out = np.zeros_like(q)
+    for s in range(0, n, B):
+        e = min(n, s + B)
+        out[s:e] = np.tril(q[s:e] @ k[s:e].T) @ v[s:e]
+    return out
+
+
+def _np_block_inclusive_prefix(q, k, v, B):
+    q = q.astype(np.float64); k = k.astype(np.float64); v = v.astype(np.float64)
+    n, d = q.shape
+    out = np.zeros_like(q)
+    S = np.zeros((d, d))
+    for s in range(0, n, B):
+        e = min(n, s + B)
+        S = S + k[s:e].T @ v[s:e]          # mistake: prefix includes the block itself
+        out[s:e] = np.tril(q[s:e] @ k[s:e].T) @ v[s:e] + q[s:e] @ S
+    return out
+
+
+def _dec_update_first(q, k, v, S0):
+    S = np.array(S0, np.float64).copy()
+    steps, units, d = q.shape
+    o = np.zeros((steps, units, d))
+    for t in range(steps):
+        for u in range(units):
+            S[u] += np.outer(k[t, u], v[t, u])
+            o[t, u] = q[t, u] @ S[u]
+    return o, S
+
+
+def _varlen_no_reset(q, k, v, cu):
+    H, T, d = q.shape
+    o = np.zeros((H, T, d))
+    for h in range(H):
+        o[h] = _np_causal(q[h], k[h], v[h])
+    return o
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+def test_mutants_are_caught():
+    strict = lambda q, k, v: _np_causal(q, k, v, strict=True)
+    transposed = lambda q, k, v: _np_causal(q, k, v, transpose_state=True)
+    good = lambda q, k, v: _np_causal(q, k, v)
+    # sanity: the straightforward numpy recurrence passes
+    pins.check_golden_causal(good)
+    pins.check_all_ones(good)
+    pins.check_one_hot(good)
+    # diagonal dropped from the mask
+    assert _fails(pins.check_golden_causal, strict)
+    assert _fails(pins.check_all_ones, strict)
+    assert _fails(pins.check_prefix_sum, strict)
+    # state used transposed (value/key roles swapped)
+    assert _fails(pins.check_golden_causal, transposed)
+    assert _fails(pins.check_one_hot, transposed)
+    # inter-block term missing, or prefix made inclusive
+    assert _fails(pins.check_golden_block, _np_block_no_inter)
+    assert _fails(pins.check_block_invariance, _np_block_no_inter, good)
+    assert _fails(pins.check_golden_block, _np_block_inclusive_prefix)
+    assert _fails(pins.check_block_invariance, _np_block_inclusive_prefix, good)
+    # decode that updates the state before reading it
+    assert _fails(pins.check_golden_decode, _dec_update_first)
+    assert _fails(pins.check_decode_vs_prefill, _dec_update_first, good)
+    # packed sequences that leak state across boundaries
+    assert _fails(pins.check_varlen_resets, _varlen_no_reset, good)
