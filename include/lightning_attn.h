@@ -1,0 +1,117 @@
+/*
+ * lightning_attn.h -- C ABI of liblightning_attn.so: the Lightning Attention
+ * forward pass (causal linear attention, block-tiled) and its constant-cost
+ * decode step, on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (wiki page "MiniMax-01 Lightning Attention", section
+ * "Lightning Attention 设计"; Tencent Cloud article "首个线性注意力架构的大模型
+ * 来了…", section 4.1):
+ *
+ *   o_i = sum_{j <= i} (q_i . k_j) v_j        for every token i of a sequence,
+ *
+ * with no scale, feature map, normaliser or decay applied inside.  The
+ * sequence is cut into blocks of `block_size` tokens; inside a block the
+ * masked left product (Q K^T) V is used, across blocks the right product
+ * Q S with S = sum of k^T v over all earlier blocks (a d x d state).
+ * The decode step is o = q S, then S += k^T v (the state read by o is the
+ * one before this token).
+ *
+ * Plain C: no C++ or HIP types in any signature.  All tensor pointers are
+ * DEVICE pointers on the current HIP device; `stream` is a hipStream_t passed
+ * as void* (NULL = the default stream).  Every launch is asynchronous on
+ * `stream`; nothing synchronises the host.  The library allocates no memory
+ * and keeps no mutable global state, so calls are reentrant; calls that share
+ * a workspace or a decode state must be ordered by the caller.
+ */
+#ifndef LIGHTNING_ATTN_H
+#define LIGHTNING_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of q, k, v and o. */
+#define LA_DTYPE_BF16 0  /* bfloat16 in, fp32 accumulation, bfloat16 out (round to nearest even) */
+#define LA_DTYPE_F32  1  /* fp32 in, fp32 accumulation, fp32 out */
+
+/* Status codes. */
+#define LA_OK           0  /* success (launches queued on the stream)               */
+#define LA_EINVAL       1  /* NULL pointer with work to do, or a negative/zero size */
+#define LA_EUNSUPPORTED 2  /* head_dim not 64/128, block_size not 64/128/256, or dtype unknown */
+#define LA_EWORKSPACE   3  /* workspace NULL or smaller than the size query returned */
+#define LA_EHIP         4  /* a HIP launch failed; see hipGetLastError semantics     */
+
+/*
+ * Bytes of device workspace lightning_attn_fwd needs for these arguments
+ * (always a multiple of 256; 0 when seq_len == 0).  `varlen` is non-zero when
+ * cu_seqlens will be passed; then `batch` is the number of packed sequences
+ * and `seq_len` their total token count.  Returns 0 for arguments
+ * lightning_attn_fwd would reject.  The workspace holds per-chunk fp32 d x d
+ * states (Tencent Cloud article, section 4.1: the compact key-value prefix of
+ * all earlier blocks) and small tables; its contents need no initialisation
+ * and are scratch after the call.
+ */
+size_t lightning_attn_fwd_workspace_size(int batch, int heads, int64_t seq_len, int head_dim,
+                                         int block_size, int varlen, int dtype);
+
+/*
+ * Number of tokens one workgroup carries the state across in the forward
+ * pass (a multiple of block_size), for the same arguments.  Informational:
+ * the result does not depend on it beyond rounding.  0 for rejected arguments.
+ */
+int64_t lightning_attn_fwd_chunk_tokens(int batch, int heads, int64_t seq_len, int head_dim,
+                                        int block_size, int varlen, int dtype);
+
+/*
+ * Forward pass (prefill).
+ *
+ * Dense input (cu_seqlens == NULL): q, k, v, o are contiguous
+ *   [batch][heads][seq_len][head_dim]; each (batch, head) is one sequence.
+ * Packed variable-length input (cu_seqlens != NULL; wiki page section
+ *   "计算优化": data-packing without padding): q, k, v, o are contiguous
+ *   [heads][seq_len][head_dim] where seq_len = T is the total token count;
+ *   cu_seqlens is a DEVICE int32 array of batch+1 entries with
+ *   cu_seqlens[0] = 0, non-decreasing, cu_seqlens[batch] = T.  Sequence s is
+ *   tokens [cu_seqlens[s], cu_seqlens[s+1]) of every head and starts from an
+ *   empty state.  These contents are a precondition, not checked.
+ *
+ * block_size in {64, 128, 256}; head_dim in {64, 128}; blocks start at each
+ * sequence's first token and the last block of a sequence may be short.
+ * o has the dtype of q and must not alias q, k, v or the workspace.
+ * workspace: device memory of at least lightning_attn_fwd_workspace_size(...)
+ * bytes (same arguments, varlen = cu_seqlens != NULL), 256-byte aligned.
+ *
+ * All argument checks happen on the host before any launch; a rejected call
+ * writes nothing.  seq_len == 0 returns LA_OK without touching any pointer.
+ * Device-side faults surface at the caller's next synchronisation.
+ */
+int lightning_attn_fwd(const void *q, const void *k, const void *v, void *o,
+                       int batch, int heads, int64_t seq_len, int head_dim, int block_size,
+                       const int32_t *cu_seqlens, int dtype,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step for batch x heads independent sequences (wiki page section
+ * "Lightning Attention 设计": inference only updates the d x d KV state,
+ * O(d^2) per token; comparison table row "状态大小").
+ *   q, k, v, o: [batch][heads][head_dim] in `dtype`;
+ *   state:      fp32 [batch][heads][head_dim][head_dim], state[a][b] with
+ *               a = key dimension, b = value dimension; read and updated in
+ *               place (caller-owned: a checkpoint is a copy of it).
+ *   o = q . state_old ;  state_new = state_old + k^T v .
+ * o must not alias the other buffers.  Checks happen on the host first.
+ */
+int lightning_attn_decode(const void *q, const void *k, const void *v, float *state, void *o,
+                          int batch, int heads, int head_dim, int dtype, void *stream);
+
+/* Static, human-readable text for a status code. */
+const char *lightning_attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIGHTNING_ATTN_H */

@@ -1,0 +1,184 @@
+"""Lightning Attention forward pass and decode step on AMD MI355X (gfx950).
+
+A thin ctypes binding over ``liblightning_attn.so``: the functions named like
+the C ABI (``lightning_attn_fwd``, ``lightning_attn_decode``, ...) only marshal
+arguments; every step of the computation runs in the library's HIP kernels.
+``fwd`` and ``decode`` are conveniences that take torch tensors, allocate the
+output and workspace with torch and launch on torch's current stream.
+
+The operation (wiki page "MiniMax-01 Lightning Attention", section
+"Lightning Attention 设计"; Tencent Cloud article section 4.1):
+    o_i = sum_{j<=i} (q_i . k_j) v_j
+computed blockwise (left product inside a block, right product with the d x d
+prefix state across blocks), and the decode step o = q S ; S += k^T v.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "LA_DTYPE_BF16", "LA_DTYPE_F32", "LA_OK", "LA_EINVAL", "LA_EUNSUPPORTED", "LA_EWORKSPACE",
+    "LA_EHIP", "LightningAttnError", "lib_path", "load_library",
+    "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_chunk_tokens", "lightning_attn_fwd",
+    "lightning_attn_decode", "lightning_attn_strerror", "fwd", "decode",
+]
+
+LA_DTYPE_BF16 = 0
+LA_DTYPE_F32 = 1
+LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EWORKSPACE, LA_EHIP = 0, 1, 2, 3, 4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class LightningAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lightning_attn_strerror(status)} (status {status})")
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "liblightning_attn.so")
+
+
+def load_library():
+    """Load the in-tree HIP library; fails loudly if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m linear_attention_attn_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.lightning_attn_fwd_workspace_size.argtypes = [i32, i32, i64, i32, i32, i32, i32]
+    lib.lightning_attn_fwd_workspace_size.restype = sz
+    lib.lightning_attn_fwd_chunk_tokens.argtypes = [i32, i32, i64, i32, i32, i32, i32]
+    lib.lightning_attn_fwd_chunk_tokens.restype = i64
+    lib.lightning_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, i32, vp, sz, vp]
+    lib.lightning_attn_fwd.restype = i32
+    lib.lightning_attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
+    lib.lightning_attn_decode.restype = i32
+    lib.lightning_attn_strerror.argtypes = [i32]
+    lib.lightning_attn_strerror.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _ptr(x):
+    """Device pointer of a tensor, an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+# ---- the C ABI, same names and argument order -----------------------------
+
+def lightning_attn_fwd_workspace_size(batch, heads, seq_len, head_dim, block_size, varlen, dtype) -> int:
+    return int(load_library().lightning_attn_fwd_workspace_size(
+        batch, heads, seq_len, head_dim, block_size, int(bool(varlen)), dtype))
+
+
+def lightning_attn_fwd_chunk_tokens(batch, heads, seq_len, head_dim, block_size, varlen, dtype) -> int:
+    return int(load_library().lightning_attn_fwd_chunk_tokens(
+        batch, heads, seq_len, head_dim, block_size, int(bool(varlen)), dtype))
+
+
+def lightning_attn_fwd(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens, dtype,
+                       workspace, workspace_bytes, stream) -> int:
+    return int(load_library().lightning_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, heads, seq_len, head_dim, block_size,
+        _ptr(cu_seqlens), dtype, _ptr(workspace), workspace_bytes, stream))
+
+
+def lightning_attn_decode(q, k, v, state, o, batch, heads, head_dim, dtype, stream) -> int:
+    return int(load_library().lightning_attn_decode(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(state), _ptr(o), batch, heads, head_dim, dtype, stream))
+
+
+def lightning_attn_strerror(status: int) -> str:
+    return load_library().lightning_attn_strerror(status).decode()
+
+
+# ---- torch conveniences -----------------------------------------------------
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return LA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return LA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_handle(device):
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_for(q, block_size: int, cu_seqlens=None):
+    """Allocate (with torch) the workspace lightning_attn_fwd needs for q's shape."""
+    import torch
+    if cu_seqlens is None:
+        batch, heads, n, d = q.shape
+        nbytes = lightning_attn_fwd_workspace_size(batch, heads, n, d, block_size, 0, _dtype_code(q))
+    else:
+        heads, n, d = q.shape
+        nbytes = lightning_attn_fwd_workspace_size(cu_seqlens.numel() - 1, heads, n, d, block_size, 1,
+                                                   _dtype_code(q))
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device), nbytes
+
+
+def fwd(q, k, v, block_size: int = 256, cu_seqlens=None, out=None, workspace=None):
+    """Causal linear attention forward on the current stream.
+
+    Dense: q, k, v [batch, heads, n, d].  Packed: q, k, v [heads, T, d] with
+    cu_seqlens an int32 device tensor of nseq+1 offsets.  Returns o (q's dtype).
+    """
+    import torch
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    if not (q.shape == k.shape == v.shape and q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share shape and dtype")
+    o = torch.empty_like(q) if out is None else out
+    if workspace is None:
+        workspace, nbytes = workspace_for(q, block_size, cu_seqlens)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    if cu_seqlens is None:
+        batch, heads, n, d = q.shape
+        cu = None
+    else:
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda:
+            raise ValueError("cu_seqlens must be an int32 device tensor")
+        heads, n, d = q.shape
+        batch = cu_seqlens.numel() - 1
+        cu = cu_seqlens
+    st = lightning_attn_fwd(q, k, v, o, batch, heads, n, d, block_size, cu, _dtype_code(q),
+                            workspace if nbytes else None, nbytes, _stream_handle(q.device))
+    if st != LA_OK:
+        raise LightningAttnError(st, "lightning_attn_fwd")
+    return o
+
+
+def decode(q, k, v, state, out=None):
+    """One decode step: o = q state_old; state += k^T v (in place).
+
+    q, k, v: [batch, heads, d]; state: fp32 [batch, heads, d, d].
+    """
+    import torch
+    if state.dtype != torch.float32 or not state.is_contiguous():
+        raise ValueError("state must be a contiguous fp32 tensor")
+    batch, heads, d = q.shape
+    if tuple(state.shape) != (batch, heads, d, d):
+        raise ValueError("state shape must be [batch, heads, d, d]")
+    o = torch.empty_like(q) if out is None else out
+    st = lightning_attn_decode(q, k, v, state, o, batch, heads, d, _dtype_code(q),
+                               _stream_handle(q.device))
+    if st != LA_OK:
+        raise LightningAttnError(st, "lightning_attn_decode")
+    return o

@@ -1,0 +1,147 @@
+// la_abi.cpp -- the extern "C" entry points of liblightning_attn.so.
+//
+// Validation, workspace planning and dispatch.  Every check runs on the host
+// before any HIP call, so a rejected call has no side effects.  The library
+// allocates nothing: the caller passes all device memory, including the
+// workspace sized by lightning_attn_fwd_workspace_size.
+#include <stdint.h>
+#include <stdlib.h>
+
+#include <algorithm>
+
+#include "../../include/lightning_attn.h"
+#include "la_internal.h"
+
+namespace la {
+
+static bool dtype_ok(int dtype) { return dtype == LA_DTYPE_BF16 || dtype == LA_DTYPE_F32; }
+
+int check_fwd_shape(int batch, int heads, int64_t seq_len, int head_dim, int block_size, int dtype) {
+    if (!dtype_ok(dtype)) return LA_EUNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return LA_EUNSUPPORTED;
+    if (block_size != 64 && block_size != 128 && block_size != 256) return LA_EUNSUPPORTED;
+    if (batch < 1 || heads < 1 || seq_len < 0) return LA_EINVAL;
+    if (heads > 65535) return LA_EUNSUPPORTED;          // heads run along grid y
+    if (seq_len > (int64_t)INT32_MAX) return LA_EUNSUPPORTED;  // int32 cu_seqlens / tables
+    return LA_OK;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int64_t env_i64(const char *name, int64_t dflt) {
+    const char *s = getenv(name);
+    if (!s || !*s) return dflt;
+    char *end = nullptr;
+    long long v = strtoll(s, &end, 10);
+    return (end && *end == 0 && v > 0) ? (int64_t)v : dflt;
+}
+
+// Chunk length: the largest power-of-two multiple of the block size (up to
+// 8192 tokens, and not beyond the average sequence) that still leaves about
+// kTargetGroups workgroups, so the chip fills while the per-chunk state
+// traffic (64 KiB of fp32 at d = 128, several times per chunk) stays small
+// against the 4 * d * 2 bytes per token of q, k, v and o.  LA_CHUNK_TOKENS
+// overrides it (rounded down to a multiple of the block size).
+void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int block_size, bool varlen,
+                   FwdPlan *plan) {
+    const int64_t kTargetGroups = env_i64("LA_TARGET_GROUPS", 2048);
+    const int64_t kMaxChunk = 8192;
+    const int64_t units = (int64_t)batch * heads;
+    const int64_t lavg = std::max<int64_t>(1, varlen ? seq_len / batch : seq_len);
+    int64_t C = block_size;
+    while (C * 2 <= kMaxChunk && C < lavg &&
+           units * ((lavg + 2 * C - 1) / (2 * C)) >= kTargetGroups)
+        C *= 2;
+    const int64_t forced = env_i64("LA_CHUNK_TOKENS", 0);
+    if (forced > 0) C = std::max<int64_t>(block_size, forced / block_size * block_size);
+
+    const int G = 32;
+    FwdPlan p;
+    p.chunk = C;
+    p.scan_group = G;
+    if (!varlen) {
+        const int64_t cps = (seq_len + C - 1) / C;
+        p.nchunk_ub = (int64_t)batch * cps;
+        p.ntile_ub = (int64_t)batch * ((cps + G - 1) / G);
+        p.scan_tiles = cps > G;
+    } else {
+        p.nchunk_ub = seq_len / C + batch;
+        p.ntile_ub = (p.nchunk_ub + G - 1) / G + batch;
+        p.scan_tiles = (seq_len + C - 1) / C > G;
+    }
+    const size_t dd = (size_t)head_dim * head_dim * sizeof(float);
+    size_t off = 0;
+    p.off_chunk_off = off;
+    off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));
+    p.off_tile_off = off;
+    off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));
+    p.off_states = off;
+    off = align256(off + (size_t)heads * (size_t)p.nchunk_ub * dd);
+    p.off_tilesum = off;
+    if (p.scan_tiles) off = align256(off + (size_t)heads * (size_t)p.ntile_ub * dd);
+    p.bytes = off;
+    *plan = p;
+}
+
+}  // namespace la
+
+extern "C" {
+
+size_t lightning_attn_fwd_workspace_size(int batch, int heads, int64_t seq_len, int head_dim,
+                                         int block_size, int varlen, int dtype) {
+    if (la::check_fwd_shape(batch, heads, seq_len, head_dim, block_size, dtype) != LA_OK) return 0;
+    if (seq_len == 0) return 0;
+    la::FwdPlan p;
+    la::make_fwd_plan(batch, heads, seq_len, head_dim, block_size, varlen != 0, &p);
+    return p.bytes;
+}
+
+int64_t lightning_attn_fwd_chunk_tokens(int batch, int heads, int64_t seq_len, int head_dim,
+                                        int block_size, int varlen, int dtype) {
+    if (la::check_fwd_shape(batch, heads, seq_len, head_dim, block_size, dtype) != LA_OK) return 0;
+    if (seq_len == 0) return 0;
+    la::FwdPlan p;
+    la::make_fwd_plan(batch, heads, seq_len, head_dim, block_size, varlen != 0, &p);
+    return p.chunk;
+}
+
+int lightning_attn_fwd(const void *q, const void *k, const void *v, void *o, int batch, int heads,
+                       int64_t seq_len, int head_dim, int block_size, const int32_t *cu_seqlens,
+                       int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    int st = la::check_fwd_shape(batch, heads, seq_len, head_dim, block_size, dtype);
+    if (st != LA_OK) return st;
+    if (seq_len == 0) return LA_OK;
+    if (!q || !k || !v || !o) return LA_EINVAL;
+    la::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.nseq = batch; a.heads = heads; a.head_dim = head_dim; a.block_size = block_size;
+    a.dtype = dtype; a.seq_len = seq_len; a.cu_seqlens = cu_seqlens;
+    la::make_fwd_plan(batch, heads, seq_len, head_dim, block_size, cu_seqlens != nullptr, &a.plan);
+    if (!workspace || workspace_bytes < a.plan.bytes) return LA_EWORKSPACE;
+    if (((uintptr_t)workspace & 255) != 0) return LA_EINVAL;
+    a.workspace = static_cast<char *>(workspace);
+    return la::launch_fwd(a, stream) == 0 ? LA_OK : LA_EHIP;
+}
+
+int lightning_attn_decode(const void *q, const void *k, const void *v, float *state, void *o, int batch,
+                          int heads, int head_dim, int dtype, void *stream) {
+    if (!(dtype == LA_DTYPE_BF16 || dtype == LA_DTYPE_F32)) return LA_EUNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return LA_EUNSUPPORTED;
+    if (batch < 1 || heads < 1) return LA_EINVAL;
+    if ((int64_t)batch * heads > (int64_t)INT32_MAX) return LA_EUNSUPPORTED;
+    if (!q || !k || !v || !state || !o) return LA_EINVAL;
+    return la::launch_decode(q, k, v, state, o, batch, heads, head_dim, dtype, stream) == 0 ? LA_OK : LA_EHIP;
+}
+
+const char *lightning_attn_strerror(int status) {
+    switch (status) {
+        case LA_OK: return "success";
+        case LA_EINVAL: return "invalid argument (null pointer with work to do, bad size or alignment)";
+        case LA_EUNSUPPORTED: return "unsupported head_dim, block_size, dtype or size";
+        case LA_EWORKSPACE: return "workspace missing or smaller than lightning_attn_fwd_workspace_size()";
+        case LA_EHIP: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

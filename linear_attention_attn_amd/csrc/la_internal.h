@@ -1,0 +1,54 @@
+// la_internal.h -- host-side plan and launcher interface shared by the C ABI
+// (la_abi.cpp) and the kernel translation units.  No HIP types here.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace la {
+
+// How a forward pass is laid out.  A "chunk" is a run of C tokens of one
+// sequence (C a multiple of the block size) that one workgroup walks block by
+// block, carrying the d x d state; chunk states are joined by a parallel
+// segmented exclusive scan.
+struct FwdPlan {
+    int64_t chunk = 0;        // C, tokens per chunk
+    int scan_group = 0;       // G, chunks per scan tile
+    int64_t nchunk_ub = 0;    // chunk slots per head (exact for dense input)
+    int64_t ntile_ub = 0;     // scan-tile slots per head
+    bool scan_tiles = false;  // some sequence may span more than G chunks
+    size_t off_chunk_off = 0; // int32 [nseq + 1]
+    size_t off_tile_off = 0;  // int32 [nseq + 1]
+    size_t off_states = 0;    // fp32 [heads][nchunk_ub][d][d]
+    size_t off_tilesum = 0;   // fp32 [heads][ntile_ub][d][d]
+    size_t bytes = 0;         // total workspace bytes
+};
+
+// Argument checks shared by the size query and the forward call.  Returns an
+// LA_* status (LA_OK when the shape is supported).
+int check_fwd_shape(int batch, int heads, int64_t seq_len, int head_dim, int block_size,
+                    int dtype);
+
+// Fill *plan for a checked shape (seq_len > 0).
+void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int block_size,
+                   bool varlen, FwdPlan *plan);
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    void *o;
+    int nseq, heads, head_dim, block_size, dtype;
+    int64_t seq_len;          // dense: tokens per sequence; packed: total tokens
+    const int32_t *cu_seqlens;  // device, or nullptr for dense input
+    char *workspace;
+    FwdPlan plan;
+};
+
+// Queue the forward kernels on `stream` (a hipStream_t).  Returns 0 or a HIP
+// error code.
+int launch_fwd(const FwdArgs &a, void *stream);
+
+// Queue one decode step.  Returns 0 or a HIP error code.
+int launch_decode(const void *q, const void *k, const void *v, float *state, void *o,
+                  int batch, int heads, int head_dim, int dtype, void *stream);
+
+}  // namespace la

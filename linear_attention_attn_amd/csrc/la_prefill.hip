@@ -1,0 +1,592 @@
+// la_prefill.hip -- Lightning Attention forward pass on gfx950.
+//
+// The method (wiki page "MiniMax-01 Lightning Attention", section "Lightning
+// Attention 设计"; Tencent Cloud article, section 4.1): cut each sequence into
+// blocks of B tokens.  Inside a block use the left product
+//     O_b^intra = mask(Q_b K_b^T) V_b          (mask keeps j <= i)
+// and across blocks the right product with the compact key-value prefix
+//     O_b = O_b^intra + Q_b S_b ,   S_b = sum over earlier blocks of K^T V .
+//
+// Kernels (all on the caller's stream, no host synchronisation):
+//   1. k_prep       chunk / scan-tile offset tables from cu_seqlens (1 WG)
+//   2. k_summary    U_c = K_c^T V_c for every chunk c of C tokens (MFMA)
+//   3. k_scan_*     fp32 exclusive prefix over chunk states, segmented at
+//                   sequence starts, as a three-phase reduce-then-scan across
+//                   chunk tiles (parallel over tiles and over the d*d lanes)
+//   4. k_fused      per chunk: start from its prefix state and walk the
+//                   chunk's blocks; per block the masked Q K^T and P V
+//                   products (MFMA, tiles staged in LDS) plus Q S, one store
+//                   of O, then S += K_b^T V_b for the next block.
+// The intra-block product and the output combine are one kernel: both
+// accumulate into the same registers (O^T = V^T P^T + S^T Q^T), so the
+// intra-block partial never goes to memory.
+#include <hip/hip_runtime.h>
+
+#include "la_common.h"
+#include "la_internal.h"
+
+namespace la {
+
+struct KParams {
+    const void *q, *k, *v;
+    void *o;
+    const int32_t *cu;      // packed offsets, or nullptr (dense)
+    int32_t *chunk_off;     // [nseq + 1]
+    int32_t *tile_off;      // [nseq + 1]
+    float *states;          // [heads][nchunk_ub][D*D]
+    float *tilesum;         // [heads][ntile_ub][D*D]
+    int64_t seq_len;        // dense: per sequence; packed: total tokens
+    int64_t chunk;          // tokens per chunk
+    int64_t nchunk_ub, ntile_ub;
+    int nseq, heads, group;
+};
+
+// ------------------------------------------------------------------ units
+
+struct Unit {
+    int64_t base;   // element offset of token 0 of this (sequence, head)
+    int64_t len;    // tokens
+};
+
+template <int D>
+__device__ __forceinline__ Unit unit_of(const KParams &p, int s, int h) {
+    Unit u;
+    if (p.cu == nullptr) {
+        u.base = ((int64_t)s * p.heads + h) * p.seq_len * D;
+        u.len = p.seq_len;
+    } else {
+        int64_t b = p.cu[s], e = p.cu[s + 1];
+        u.base = ((int64_t)h * p.seq_len + b) * D;
+        u.len = e - b;
+    }
+    return u;
+}
+
+// Largest s in [0, n) with off[s] <= x (off non-decreasing, off[0] = 0).
+__device__ __forceinline__ int find_seg(const int32_t *off, int n, int64_t x) {
+    int lo = 0, hi = n;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if ((int64_t)off[mid] <= x) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// -------------------------------------------------------------- k_prep
+// chunk_off[s] = sum_{s' < s} ceil(L_s' / C);  tile_off[s] = sum ceil(nc_s' / G).
+constexpr int kPrepThreads = 1024;
+
+__global__ __launch_bounds__(kPrepThreads) void k_prep(KParams p) {
+    __shared__ int64_t sc[kPrepThreads], st[kPrepThreads];
+    const int t = threadIdx.x;
+    const int per = (p.nseq + kPrepThreads - 1) / kPrepThreads;
+    const int s0 = t * per, s1 = min(p.nseq, s0 + per);
+    int64_t c = 0, g = 0;
+    for (int s = s0; s < s1; ++s) {
+        int64_t L = p.cu ? (int64_t)p.cu[s + 1] - p.cu[s] : p.seq_len;
+        int64_t nc = (L + p.chunk - 1) / p.chunk;
+        c += nc;
+        g += (nc + p.group - 1) / p.group;
+    }
+    sc[t] = c; st[t] = g;
+    __syncthreads();
+    for (int d = 1; d < kPrepThreads; d <<= 1) {   // inclusive Hillis-Steele scan
+        int64_t a = t >= d ? sc[t - d] : 0, b = t >= d ? st[t - d] : 0;
+        __syncthreads();
+        sc[t] += a; st[t] += b;
+        __syncthreads();
+    }
+    c = t ? sc[t - 1] : 0;
+    g = t ? st[t - 1] : 0;
+    for (int s = s0; s < s1; ++s) {
+        p.chunk_off[s] = (int32_t)c;
+        p.tile_off[s] = (int32_t)g;
+        int64_t L = p.cu ? (int64_t)p.cu[s + 1] - p.cu[s] : p.seq_len;
+        int64_t nc = (L + p.chunk - 1) / p.chunk;
+        c += nc;
+        g += (nc + p.group - 1) / p.group;
+    }
+    if (t == kPrepThreads - 1) {
+        p.chunk_off[p.nseq] = (int32_t)sc[t];
+        p.tile_off[p.nseq] = (int32_t)st[t];
+    }
+}
+
+// ---------------------------------------------------------- tile config
+
+template <typename T, int D, int BLK>
+struct Cfg {
+    static constexpr int ES = Elem<T>::kBytes;
+    static constexpr int NW = 8, NT = NW * kWave;
+    static constexpr int TJ = ES == 2 ? 64 : 32;        // K/V tokens per LDS tile
+    static constexpr int EPC = 16 / ES;                 // elements per 16-byte chunk
+    static constexpr int KR_ROW = D * ES;               // row-major K row bytes
+    static constexpr int KT_ROW = TJ * ES;              // transposed row bytes (128)
+    static constexpr int ST_ROW = D * ES;
+    static constexpr int KR_BYTES = TJ * KR_ROW;
+    static constexpr int KT_BYTES = D * KT_ROW;
+    static constexpr int ST_BYTES = D * ST_ROW;
+    static constexpr int NP = (TJ / 4) * (D / EPC);     // 4-token patches per tensor tile
+    static constexpr int DT = D / 16;                   // 16-wide tiles along d
+    static constexpr int KC = D / 32;                   // 32-wide k steps along d
+    // state tiles per wave: SA x SB of the DT x DT grid
+    static constexpr int SA = D == 128 ? 2 : 1;
+    static constexpr int SB = D == 128 ? 4 : 2;
+    static constexpr int AW = DT / SA;                  // waves along a
+    // row slabs (16 rows) of a block handled per wave, and the column split
+    static constexpr int NSW = BLK == 64 ? 1 : 2;
+    static constexpr int CSPLIT = BLK == 256 ? 1 : 2;
+    static constexpr int NCT = DT / CSPLIT;             // 16-wide output column tiles per wave
+    static_assert(NP <= 256, "patch mapping");
+    static_assert(AW * (DT / SB) == NW, "state split");
+    static_assert(BLK % TJ == 0, "tile");
+};
+
+// Row slab (0..BLK/16-1) handled as slab `s` by wave w: pairs of slabs from
+// both ends of the block so that every wave does the same causal work.
+template <int BLK>
+__device__ __forceinline__ int slab_of(int w, int s) {
+    if constexpr (BLK == 256) return s == 0 ? w : 15 - w;
+    else if constexpr (BLK == 128) return s == 0 ? (w & 3) : 7 - (w & 3);
+    else return w & 3;
+}
+
+// ------------------------------------------------------ tile staging
+// Each of the first NP threads owns a 4-token x 16-byte patch of K, the
+// threads [256, 256 + NP) the same patch of V.  The patch is loaded with four
+// 16-byte global loads (coalesced along d), written to LDS row-major (K
+// only, for Q K^T) and transposed (token-contiguous rows, for the products
+// that reduce over tokens).
+template <typename T, int D>
+struct Patch {
+    u32x4_t x[4];
+};
+
+template <typename T, int D, int BLK>
+__device__ __forceinline__ void patch_load(Patch<T, D> &pt, const T *kbase, const T *vbase,
+                                           int64_t tok0, int64_t tend) {
+    using C = Cfg<T, D, BLK>;
+    const int t = threadIdx.x;
+    const bool isk = t < C::NP;
+    const bool isv = t >= 256 && t < 256 + C::NP;
+    const int pi = isk ? t : t - 256;
+    const int tg = pi / (D / C::EPC), ch = pi % (D / C::EPC);
+    const T *src = isk ? kbase : vbase;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int64_t tok = tok0 + 4 * tg + r;
+        const bool ok = (isk || isv) && tok < tend;
+        pt.x[r] = ok ? *reinterpret_cast<const u32x4_t *>(src + tok * D + ch * C::EPC)
+                     : u32x4_t{0u, 0u, 0u, 0u};
+    }
+}
+
+template <typename T, int D, int BLK, bool kWithRowMajor>
+__device__ __forceinline__ void patch_store(const Patch<T, D> &pt, char *kr, char *kt, char *vt) {
+    using C = Cfg<T, D, BLK>;
+    const int t = threadIdx.x;
+    const bool isk = t < C::NP;
+    const bool isv = t >= 256 && t < 256 + C::NP;
+    if (!isk && !isv) return;
+    const int pi = isk ? t : t - 256;
+    const int tg = pi / (D / C::EPC), ch = pi % (D / C::EPC);
+    if (kWithRowMajor && isk) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<u32x4_t *>(kr + LdsRows<C::KR_ROW>::off(4 * tg + r, ch * 16)) = pt.x[r];
+    }
+    char *dst = isk ? kt : vt;
+    if constexpr (C::ES == 2) {
+        // element e of token r sits in dword e/2, half e%2, of pt.x[r]
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int dw = e >> 1;
+            uint32_t lo, hi;
+            if (e & 1) {
+                lo = (pt.x[0][dw] >> 16) | (pt.x[1][dw] & 0xffff0000u);
+                hi = (pt.x[2][dw] >> 16) | (pt.x[3][dw] & 0xffff0000u);
+            } else {
+                lo = (pt.x[0][dw] & 0xffffu) | (pt.x[1][dw] << 16);
+                hi = (pt.x[2][dw] & 0xffffu) | (pt.x[3][dw] << 16);
+            }
+            *reinterpret_cast<u32x2_t *>(dst + LdsRows<C::KT_ROW>::off(ch * 8 + e, 4 * tg * 2)) =
+                u32x2_t{lo, hi};
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<u32x4_t *>(dst + LdsRows<C::KT_ROW>::off(ch * 4 + e, 4 * tg * 4)) =
+                u32x4_t{pt.x[0][e], pt.x[1][e], pt.x[2][e], pt.x[3][e]};
+    }
+}
+
+// S[ia][ib] += K^T V over one LDS tile (TJ tokens).  Wave w owns the state
+// tiles a in [a0, a0+SA), b in [b0, b0+SB) (16 x 16 each).
+template <typename T, int D, int BLK, int SA, int SB>
+__device__ __forceinline__ void state_update(f32x4_t (&S)[SA][SB], const char *kt, const char *vt,
+                                             int a0, int b0) {
+    using C = Cfg<T, D, BLK>;
+    static_assert(SA == C::SA && SB == C::SB, "state split");
+    const int l = lane_id(), c = l & 15, g = l >> 4;
+#pragma unroll
+    for (int jg = 0; jg < C::TJ / 32; ++jg) {
+        Frag<T> A[C::SA], B[C::SB];
+#pragma unroll
+        for (int ia = 0; ia < C::SA; ++ia)
+            A[ia] = lds_read8<T, C::KT_ROW>(kt, (a0 + ia) * 16 + c, jg * 32 + 8 * g);
+#pragma unroll
+        for (int ib = 0; ib < C::SB; ++ib)
+            B[ib] = lds_read8<T, C::KT_ROW>(vt, (b0 + ib) * 16 + c, jg * 32 + 8 * g);
+#pragma unroll
+        for (int ia = 0; ia < C::SA; ++ia)
+#pragma unroll
+            for (int ib = 0; ib < C::SB; ++ib) mma(S[ia][ib], A[ia], B[ib]);
+    }
+}
+
+// --------------------------------------------------------- k_summary
+// states[h][chunk] = K_c^T V_c  (fp32, row a = key dim, column b = value dim)
+template <typename T, int D, int BLK>
+__global__ __launch_bounds__(512, 2) void k_summary(KParams p) {
+    using C = Cfg<T, D, BLK>;
+    __shared__ __attribute__((aligned(16))) char lds[2][2 * C::KT_BYTES];
+    const int h = blockIdx.y;
+    const int64_t gch = blockIdx.x;
+    if (gch >= p.chunk_off[p.nseq]) return;
+    const int s = find_seg(p.chunk_off, p.nseq, gch);
+    const Unit u = unit_of<D>(p, s, h);
+    const int64_t t0 = (gch - p.chunk_off[s]) * p.chunk;
+    const int64_t t1 = min(u.len, t0 + p.chunk);
+    const T *kb = reinterpret_cast<const T *>(p.k) + u.base;
+    const T *vb = reinterpret_cast<const T *>(p.v) + u.base;
+
+    const int w = wave_id(), l = lane_id(), c = l & 15, g = l >> 4;
+    const int a0 = C::SA * (w % C::AW), b0 = C::SB * (w / C::AW);
+    f32x4_t S[C::SA][C::SB];
+#pragma unroll
+    for (int ia = 0; ia < C::SA; ++ia)
+#pragma unroll
+        for (int ib = 0; ib < C::SB; ++ib) S[ia][ib] = zero4();
+
+    const int64_t ntile = (t1 - t0 + C::TJ - 1) / C::TJ;
+    Patch<T, D> pt;
+    patch_load<T, D, BLK>(pt, kb, vb, t0, t1);
+    patch_store<T, D, BLK, false>(pt, nullptr, lds[0], lds[0] + C::KT_BYTES);
+    __syncthreads();
+    for (int64_t it = 0; it < ntile; ++it) {
+        const int buf = it & 1;
+        if (it + 1 < ntile) patch_load<T, D, BLK>(pt, kb, vb, t0 + (it + 1) * C::TJ, t1);
+        state_update<T, D, BLK, C::SA, C::SB>(S, lds[buf], lds[buf] + C::KT_BYTES, a0, b0);
+        if (it + 1 < ntile)
+            patch_store<T, D, BLK, false>(pt, nullptr, lds[buf ^ 1], lds[buf ^ 1] + C::KT_BYTES);
+        __syncthreads();
+    }
+    float *dst = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
+#pragma unroll
+    for (int ia = 0; ia < C::SA; ++ia)
+#pragma unroll
+        for (int ib = 0; ib < C::SB; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c] = S[ia][ib][r];
+}
+
+// ------------------------------------------------------------- scans
+// Exclusive prefix over the chunks of every (sequence, head), in place on
+// `states`.  Lanes are the d*d state entries; chunk tiles of G chunks are
+// reduced (A), the tile totals scanned per sequence (B), and each tile
+// rescanned from its prefix (C).  With every sequence inside one tile only
+// phase C runs.
+constexpr int kScanThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kScanThreads) void k_scan_reduce(KParams p) {
+    const int h = blockIdx.z;
+    const int64_t tile = blockIdx.x;
+    if (tile >= p.tile_off[p.nseq]) return;
+    const int s = find_seg(p.tile_off, p.nseq, tile);
+    const int64_t c0 = p.chunk_off[s] + (tile - p.tile_off[s]) * p.group;
+    const int64_t c1 = min((int64_t)p.chunk_off[s + 1], c0 + p.group);
+    const int e = blockIdx.y * kScanThreads + threadIdx.x;
+    const float *src = p.states + (int64_t)h * p.nchunk_ub * (D * D) + e;
+    float acc = 0.f;
+    for (int64_t c = c0; c < c1; ++c) acc += src[c * (D * D)];
+    p.tilesum[((int64_t)h * p.ntile_ub + tile) * (D * D) + e] = acc;
+}
+
+template <int D>
+__global__ __launch_bounds__(kScanThreads) void k_scan_tiles(KParams p) {
+    const int h = blockIdx.z, s = blockIdx.x;
+    const int e = blockIdx.y * kScanThreads + threadIdx.x;
+    float *ts = p.tilesum + (int64_t)h * p.ntile_ub * (D * D) + e;
+    float run = 0.f;
+    for (int64_t t = p.tile_off[s]; t < p.tile_off[s + 1]; ++t) {
+        const float x = ts[t * (D * D)];
+        ts[t * (D * D)] = run;
+        run += x;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kScanThreads) void k_scan_apply(KParams p, int use_tiles) {
+    const int h = blockIdx.z;
+    const int64_t tile = blockIdx.x;
+    if (tile >= p.tile_off[p.nseq]) return;
+    const int s = find_seg(p.tile_off, p.nseq, tile);
+    const int64_t c0 = p.chunk_off[s] + (tile - p.tile_off[s]) * p.group;
+    const int64_t c1 = min((int64_t)p.chunk_off[s + 1], c0 + p.group);
+    const int e = blockIdx.y * kScanThreads + threadIdx.x;
+    float *st = p.states + (int64_t)h * p.nchunk_ub * (D * D) + e;
+    float run = use_tiles ? p.tilesum[((int64_t)h * p.ntile_ub + tile) * (D * D) + e] : 0.f;
+    for (int64_t c = c0; c < c1; ++c) {
+        const float x = st[c * (D * D)];
+        st[c * (D * D)] = run;
+        run += x;
+    }
+}
+
+// ----------------------------------------------------------- k_fused
+template <typename T, int D, int BLK>
+__global__ __launch_bounds__(512, 1) void k_fused(KParams p) {
+    using C = Cfg<T, D, BLK>;
+    constexpr int NBUF = (C::ES == 4 && D == 128) ? 1 : 2;
+    constexpr int BUF = C::KR_BYTES + 2 * C::KT_BYTES;
+    __shared__ __attribute__((aligned(16))) char lds[NBUF * BUF + C::ST_BYTES];
+    char *const st = lds + NBUF * BUF;
+
+    const int h = blockIdx.y;
+    const int64_t gch = blockIdx.x;
+    if (gch >= p.chunk_off[p.nseq]) return;
+    const int s = find_seg(p.chunk_off, p.nseq, gch);
+    const Unit u = unit_of<D>(p, s, h);
+    const int64_t cl = gch - p.chunk_off[s];
+    const int64_t t0 = cl * p.chunk;
+    const int64_t t1 = min(u.len, t0 + p.chunk);
+    const T *qb = reinterpret_cast<const T *>(p.q) + u.base;
+    const T *kb = reinterpret_cast<const T *>(p.k) + u.base;
+    const T *vb = reinterpret_cast<const T *>(p.v) + u.base;
+    T *ob = reinterpret_cast<T *>(p.o) + u.base;
+
+    const int w = wave_id(), l = lane_id(), c = l & 15, g = l >> 4;
+    const int a0 = C::SA * (w % C::AW), b0 = C::SB * (w / C::AW);
+    const int ct0 = C::CSPLIT == 1 ? 0 : (w >> 2) * C::NCT;
+
+    // ---- state at the chunk start (exclusive prefix from the scan)
+    f32x4_t S[C::SA][C::SB];
+    {
+        const float *src = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
+        const bool first = cl == 0;
+#pragma unroll
+        for (int ia = 0; ia < C::SA; ++ia)
+#pragma unroll
+            for (int ib = 0; ib < C::SB; ++ib)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    S[ia][ib][r] = first ? 0.f : src[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c];
+#pragma unroll
+        for (int ia = 0; ia < C::SA; ++ia)
+#pragma unroll
+            for (int ib = 0; ib < C::SB; ++ib)
+                lds_write4<T, C::ST_ROW>(st, (b0 + ib) * 16 + c, (a0 + ia) * 16 + 4 * g, S[ia][ib]);
+    }
+
+    const int64_t nblk = (t1 - t0 + BLK - 1) / BLK;
+    Patch<T, D> pt;
+    patch_load<T, D, BLK>(pt, kb, vb, t0, t1);
+    patch_store<T, D, BLK, true>(pt, lds, lds + C::KR_BYTES, lds + C::KR_BYTES + C::KT_BYTES);
+
+    // Q fragments of this wave's row slabs: row 16*slab + c, d = 32*kc + 8g .. +7
+    Frag<T> Q[C::NSW][C::KC];
+    auto load_q = [&](int64_t tb) {
+#pragma unroll
+        for (int si = 0; si < C::NSW; ++si) {
+            const int64_t row = tb + 16 * slab_of<BLK>(w, si) + c;
+            const bool ok = row < t1;
+#pragma unroll
+            for (int kc = 0; kc < C::KC; ++kc)
+                Q[si][kc] = gload8<T>(qb + row * D + kc * 32 + 8 * g, ok);
+        }
+    };
+    load_q(t0);
+    __syncthreads();
+
+    int buf = 0;
+    for (int64_t bi = 0; bi < nblk; ++bi) {
+        const int64_t tb = t0 + bi * BLK;
+        const int bl = (int)min((int64_t)BLK, t1 - tb);
+        const int ntj = (bl + C::TJ - 1) / C::TJ;
+        const bool more = bi + 1 < nblk;
+
+        // ---- inter-block right product with the block-start state: O^T = S^T Q^T
+        f32x4_t O[C::NSW][C::NCT];
+#pragma unroll
+        for (int si = 0; si < C::NSW; ++si)
+#pragma unroll
+            for (int t = 0; t < C::NCT; ++t) O[si][t] = zero4();
+#pragma unroll
+        for (int t = 0; t < C::NCT; ++t)
+#pragma unroll
+            for (int kc = 0; kc < C::KC; ++kc) {
+                const Frag<T> A = lds_read8<T, C::ST_ROW>(st, (ct0 + t) * 16 + c, kc * 32 + 8 * g);
+#pragma unroll
+                for (int si = 0; si < C::NSW; ++si) mma(O[si][t], A, Q[si][kc]);
+            }
+
+        for (int jt = 0; jt < ntj; ++jt) {
+            const char *kr = lds + buf * BUF;
+            const char *kt = kr + C::KR_BYTES;
+            const char *vt = kt + C::KT_BYTES;
+            // prefetch the next tile of the chunk (next block's first tile at the end)
+            const bool last = jt + 1 == ntj;
+            const bool nxt = !last || more;
+            const int64_t ntok = last ? tb + BLK : tb + (jt + 1) * C::TJ;
+            if (nxt) patch_load<T, D, BLK>(pt, kb, vb, ntok, t1);
+
+            // ---- intra-block left product for this K/V tile
+#pragma unroll
+            for (int jg = 0; jg < C::TJ / 32; ++jg) {
+                const int jb = jt * C::TJ + jg * 32;      // block-local first token of the group
+                f32x4_t P[C::NSW][2];
+                bool need[C::NSW], need1[C::NSW];
+#pragma unroll
+                for (int si = 0; si < C::NSW; ++si) {
+                    const int i0 = 16 * slab_of<BLK>(w, si);
+                    need[si] = jb <= i0 + 15;
+                    need1[si] = jb + 16 <= i0 + 15;
+                    P[si][0] = zero4();
+                    P[si][1] = zero4();
+                }
+                // P^T = K Q^T : rows j (this group), columns i (the slab)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    bool any = false;
+#pragma unroll
+                    for (int si = 0; si < C::NSW; ++si) any |= hh ? need1[si] : need[si];
+                    if (!any) continue;
+#pragma unroll
+                    for (int kc = 0; kc < C::KC; ++kc) {
+                        const Frag<T> A = lds_read8<T, C::KR_ROW>(kr, jg * 32 + 16 * hh + c, kc * 32 + 8 * g);
+#pragma unroll
+                        for (int si = 0; si < C::NSW; ++si)
+                            if (hh ? need1[si] : need[si]) mma(P[si][hh], A, Q[si][kc]);
+                    }
+                }
+                Frag<T> PF[C::NSW];
+#pragma unroll
+                for (int si = 0; si < C::NSW; ++si) {
+                    const int i0 = 16 * slab_of<BLK>(w, si);
+                    const int i = i0 + c;                          // block-local query row
+                    if (need[si] && jb + 31 > i0) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            if (jb + 4 * g + r > i) P[si][0][r] = 0.f;
+                            if (jb + 16 + 4 * g + r > i) P[si][1][r] = 0.f;
+                        }
+                    }
+                    PF[si] = frag_from_f32(P[si][0], P[si][1], T{});
+                }
+                // O^T += V^T P^T : k-slots (4g..4g+3) and (16+4g..16+4g+3) of the group
+                bool anyg = false;
+#pragma unroll
+                for (int si = 0; si < C::NSW; ++si) anyg |= need[si];
+                if (anyg) {
+#pragma unroll
+                    for (int t = 0; t < C::NCT; ++t) {
+                        const Frag<T> A = lds_read4x2<T, C::KT_ROW>(vt, (ct0 + t) * 16 + c,
+                                                                    jg * 32 + 4 * g, jg * 32 + 16 + 4 * g);
+#pragma unroll
+                        for (int si = 0; si < C::NSW; ++si)
+                            if (need[si]) mma(O[si][t], A, PF[si]);
+                    }
+                }
+            }
+            // Q of this block is dead after the last tile's scores: fetch the next block's
+            if (last && more) load_q(tb + BLK);
+            // ---- state for the next block of this chunk
+            if (more) state_update<T, D, BLK, C::SA, C::SB>(S, kt, vt, a0, b0);
+
+            if (nxt) {
+                if (NBUF == 1) __syncthreads();
+                char *nk = lds + (NBUF == 2 ? (buf ^ 1) : 0) * BUF;
+                patch_store<T, D, BLK, true>(pt, nk, nk + C::KR_BYTES, nk + C::KR_BYTES + C::KT_BYTES);
+            }
+            __syncthreads();
+            if (NBUF == 2) buf ^= 1;
+        }
+
+        // ---- store O: lane holds row (16*slab + c), columns 16*t + 4g .. +3
+#pragma unroll
+        for (int si = 0; si < C::NSW; ++si) {
+            const int64_t row = tb + 16 * slab_of<BLK>(w, si) + c;
+            if (row < t1) {
+#pragma unroll
+                for (int t = 0; t < C::NCT; ++t) store4(ob + row * D + (ct0 + t) * 16 + 4 * g, O[si][t]);
+            }
+        }
+        if (more) {
+            // every wave read the old state copy before the tile loop's barriers
+#pragma unroll
+            for (int ia = 0; ia < C::SA; ++ia)
+#pragma unroll
+                for (int ib = 0; ib < C::SB; ++ib)
+                    lds_write4<T, C::ST_ROW>(st, (b0 + ib) * 16 + c, (a0 + ia) * 16 + 4 * g, S[ia][ib]);
+            __syncthreads();
+        }
+    }
+}
+
+// -------------------------------------------------------------- host side
+
+template <typename T, int D, int BLK>
+static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream_t st) {
+    const dim3 gchunks((unsigned)plan.nchunk_ub, (unsigned)kp.heads);
+    hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, st, kp);
+    hipLaunchKernelGGL((k_summary<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
+    const dim3 gtiles((unsigned)plan.ntile_ub, (D * D) / kScanThreads, (unsigned)kp.heads);
+    if (plan.scan_tiles) {
+        hipLaunchKernelGGL(k_scan_reduce<D>, gtiles, dim3(kScanThreads), 0, st, kp);
+        hipLaunchKernelGGL(k_scan_tiles<D>, dim3(kp.nseq, (D * D) / kScanThreads, kp.heads),
+                           dim3(kScanThreads), 0, st, kp);
+    }
+    hipLaunchKernelGGL(k_scan_apply<D>, gtiles, dim3(kScanThreads), 0, st, kp, plan.scan_tiles ? 1 : 0);
+    hipLaunchKernelGGL((k_fused<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_blk(const KParams &kp, const FwdPlan &plan, int blk, hipStream_t st) {
+    switch (blk) {
+        case 64: return launch_typed<T, D, 64>(kp, plan, st);
+        case 128: return launch_typed<T, D, 128>(kp, plan, st);
+        default: return launch_typed<T, D, 256>(kp, plan, st);
+    }
+}
+
+int launch_fwd(const FwdArgs &a, void *stream) {
+    KParams kp;
+    kp.q = a.q; kp.k = a.k; kp.v = a.v; kp.o = a.o;
+    kp.cu = a.cu_seqlens;
+    kp.chunk_off = reinterpret_cast<int32_t *>(a.workspace + a.plan.off_chunk_off);
+    kp.tile_off = reinterpret_cast<int32_t *>(a.workspace + a.plan.off_tile_off);
+    kp.states = reinterpret_cast<float *>(a.workspace + a.plan.off_states);
+    kp.tilesum = reinterpret_cast<float *>(a.workspace + a.plan.off_tilesum);
+    kp.seq_len = a.seq_len;
+    kp.chunk = a.plan.chunk;
+    kp.nchunk_ub = a.plan.nchunk_ub;
+    kp.ntile_ub = a.plan.ntile_ub;
+    kp.nseq = a.nseq;
+    kp.heads = a.heads;
+    kp.group = a.plan.scan_group;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (a.dtype == 0) {
+        e = a.head_dim == 64 ? launch_blk<bf16_t, 64>(kp, a.plan, a.block_size, st)
+                             : launch_blk<bf16_t, 128>(kp, a.plan, a.block_size, st);
+    } else {
+        e = a.head_dim == 64 ? launch_blk<float, 64>(kp, a.plan, a.block_size, st)
+                             : launch_blk<float, 128>(kp, a.plan, a.block_size, st);
+    }
+    return (int)e;
+}
+
+}  // namespace la

@@ -1,0 +1,66 @@
+"""Helpers for the GPU parity tests (HIP path vs the CPU oracle)."""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+
+TOL = {"bf16": 1e-2, "f32": 1e-4}
+
+
+def note(msg):
+    """Name the case before a GPU step (flushed, so it survives a crash)."""
+    sys.stdout.write(f"[gpu-case] {msg}\n")
+    sys.stdout.flush()
+
+
+def device():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import linear_attention_attn_amd as la
+    la.load_library()   # raises if the HIP library is missing: no silent fallback
+    return torch.device("cuda:0")
+
+
+def torch_dtype(name):
+    import torch
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
+
+
+def randn_qkv(shape, dtype, seed, dev):
+    """q, k ~ N(0,1)/sqrt(d), v ~ N(0,1), rounded to dtype (device tensors)."""
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    d = shape[-1]
+    q = (torch.randn(shape, generator=g, device=dev) / math.sqrt(d)).to(torch_dtype(dtype))
+    k = (torch.randn(shape, generator=g, device=dev) / math.sqrt(d)).to(torch_dtype(dtype))
+    v = torch.randn(shape, generator=g, device=dev).to(torch_dtype(dtype))
+    return q, k, v
+
+
+def host(x):
+    import torch
+    return x.detach().to("cpu").to(torch.float32).numpy()
+
+
+class chunk_tokens:
+    """Temporarily force the library's chunk length (LA_CHUNK_TOKENS)."""
+
+    def __init__(self, n):
+        self.n = n
+
+    def __enter__(self):
+        self.old = os.environ.get("LA_CHUNK_TOKENS")
+        if self.n:
+            os.environ["LA_CHUNK_TOKENS"] = str(self.n)
+        else:
+            os.environ.pop("LA_CHUNK_TOKENS", None)
+
+    def __exit__(self, *a):
+        if self.old is None:
+            os.environ.pop("LA_CHUNK_TOKENS", None)
+        else:
+            os.environ["LA_CHUNK_TOKENS"] = self.old

@@ -1,0 +1,114 @@
+"""C-ABI library on the host (no GPU): it loads, exports every declared symbol,
+sizes workspaces, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", fn)).read()
+            txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+            names += re.findall(r"\b(lightning_attn_\w+)\s*\(", txt)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def la():
+    import linear_attention_attn_amd as m
+    if not os.path.exists(m.lib_path()):
+        from linear_attention_attn_amd import build
+        build.build()
+    m.load_library()
+    return m
+
+
+def test_exports_every_declared_symbol(la):
+    names = _declared_functions()
+    assert {"lightning_attn_fwd", "lightning_attn_decode", "lightning_attn_fwd_workspace_size",
+            "lightning_attn_strerror"} <= set(names)
+    lib = ctypes.CDLL(la.lib_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_names_match_abi(la):
+    for n in _declared_functions():
+        assert callable(getattr(la, n)), n
+
+
+def test_strerror(la):
+    assert la.lightning_attn_strerror(la.LA_OK) == "success"
+    for s in (la.LA_EINVAL, la.LA_EUNSUPPORTED, la.LA_EWORKSPACE, la.LA_EHIP):
+        assert la.lightning_attn_strerror(s) not in ("success", "unknown status")
+    assert la.lightning_attn_strerror(99) == "unknown status"
+
+
+def test_workspace_size(la):
+    ws = la.lightning_attn_fwd_workspace_size
+    assert ws(1, 1, 0, 128, 256, 0, 0) == 0
+    assert ws(1, 1, 100, 96, 256, 0, 0) == 0             # rejected shape
+    a = ws(4, 64, 8192, 128, 256, 0, 0)
+    assert a > 0 and a % 256 == 0
+    # per-chunk fp32 d x d states dominate: at least one per (sequence, head, chunk)
+    C = la.lightning_attn_fwd_chunk_tokens(4, 64, 8192, 128, 256, 0, 0)
+    assert C % 256 == 0 and C >= 256
+    assert a >= 4 * 64 * (8192 // C) * 128 * 128 * 4
+    # packed layout needs room for the worst-case chunk count
+    b = ws(16, 64, 368523, 128, 256, 1, 0)
+    C = la.lightning_attn_fwd_chunk_tokens(16, 64, 368523, 128, 256, 1, 0)
+    assert b >= 64 * (368523 // C + 16) * 128 * 128 * 4
+
+
+@pytest.mark.parametrize("args,expect", [
+    # (batch, heads, seq_len, head_dim, block_size, dtype)
+    ((1, 1, 10, 96, 64, 0), 2),       # head_dim unsupported
+    ((1, 1, 10, 64, 100, 0), 2),      # block_size unsupported
+    ((1, 1, 10, 64, 64, 7), 2),       # dtype unknown
+    ((0, 1, 10, 64, 64, 0), 1),       # batch < 1
+    ((1, 0, 10, 64, 64, 0), 1),       # heads < 1
+    ((1, 1, -1, 64, 64, 0), 1),       # negative length
+])
+def test_fwd_rejects_shapes(la, args, expect):
+    b, h, n, d, B, dt = args
+    assert la.lightning_attn_fwd(None, None, None, None, b, h, n, d, B, None, dt, None, 0, None) == expect
+
+
+def test_fwd_zero_length_is_noop(la):
+    assert la.lightning_attn_fwd(None, None, None, None, 1, 1, 0, 64, 64, None, 0, None, 0, None) == 0
+
+
+def test_fwd_null_pointers_and_workspace(la):
+    fake = 1 << 20  # never dereferenced: every check below fails before a launch
+    assert la.lightning_attn_fwd(None, fake, fake, fake, 1, 1, 10, 64, 64, None, 0, fake, 1 << 30, None) == 1
+    assert la.lightning_attn_fwd(fake, fake, fake, None, 1, 1, 10, 64, 64, None, 0, fake, 1 << 30, None) == 1
+    need = la.lightning_attn_fwd_workspace_size(1, 1, 10, 64, 64, 0, 0)
+    assert la.lightning_attn_fwd(fake, fake, fake, fake, 1, 1, 10, 64, 64, None, 0, None, need, None) == 3
+    assert la.lightning_attn_fwd(fake, fake, fake, fake, 1, 1, 10, 64, 64, None, 0, fake, need - 1, None) == 3
+    # misaligned workspace
+    assert la.lightning_attn_fwd(fake, fake, fake, fake, 1, 1, 10, 64, 64, None, 0, fake + 8, need, None) == 1
+
+
+def test_decode_rejects(la):
+    fake = 1 << 20
+    assert la.lightning_attn_decode(fake, fake, fake, fake, fake, 1, 1, 96, 0, None) == 2
+    assert la.lightning_attn_decode(fake, fake, fake, fake, fake, 1, 1, 64, 3, None) == 2
+    assert la.lightning_attn_decode(fake, fake, fake, fake, fake, 0, 1, 64, 0, None) == 1
+    assert la.lightning_attn_decode(fake, fake, fake, None, fake, 1, 1, 64, 0, None) == 1
+
+
+def test_product_never_imports_oracle():
+    """The HIP path must not route through the CPU oracle."""
+    pkg = os.path.join(ROOT, "linear_attention_attn_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f
+                assert "la_oracle" not in txt, f
