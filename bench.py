@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the Lightning Attention forward pass (prefill) on one MI355X.
+
+One step = one full forward pass (every kernel of the path) over the
+MiniMax-layer workload: batch 4, 64 heads, 8192 tokens, head_dim 128, block
+256, bf16 in / fp32 accumulation / bf16 out, synthetic N(0,1) inputs already
+resident in HBM.  Prints ONE JSON line on stdout.
+
+Also reported in the same line (extra keys): per-kernel times from HIP events
+recorded on the library's stream, the decode step's achieved GB/s (256
+sequences x 64 heads, fp32 state, 128 steps), the 1,048,576-token prefill,
+and the CPU oracle timed on a bounded sample of the same prefill workload.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "prefill tokens/s + TFLOP/s (% bf16 MFMA peak) at 64 heads, d=128; decode GB/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles created through the HIP runtime (for the library's
+    stage markers, recorded on the stream the kernels run on)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.lib.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            out.append(e.value)
+        return out
+
+    def ms(self, a, b):
+        f = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(f), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return f.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.lib.hipEventDestroy(e)
+
+
+def prefill_flops_per_head_token(d, B):
+    """Algorithmic work: 2d^2 (Q S) + 2d^2 (K^T V) + 2d(B+1) (causal half of the
+    intra-block Q K^T and P V, diagonal included)."""
+    return 4 * d * d + 2 * d * (B + 1)
+
+
+def bench_prefill(w, steps, warmup, dev, traced=True):
+    import torch
+    import linear_attention_attn_amd as la
+    import synth
+
+    q, k, v = synth.prefill_inputs(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype, w.cid, dev)
+    o = torch.empty_like(q)
+    code = la.LA_DTYPE_BF16 if w.dtype == "bf16" else la.LA_DTYPE_F32
+    nbytes = la.lightning_attn_fwd_workspace_size(w.batch, w.heads, w.seq_len, w.head_dim,
+                                                  w.block_size, 0, code)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    args = (q, k, v, o, w.batch, w.heads, w.seq_len, w.head_dim, w.block_size, None, code, ws,
+            nbytes, stream)
+
+    def step():
+        st = la.lightning_attn_fwd(*args)
+        if st != la.LA_OK:
+            raise la.LightningAttnError(st, "lightning_attn_fwd")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    hip = HipEvents()
+    evs = [hip.create(la.LA_FWD_NUM_EVENTS) for _ in range(steps)] if traced else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if traced:
+            st = la.lightning_attn_fwd_traced(*args, evs[i], la.LA_FWD_NUM_EVENTS)
+            if st != la.LA_OK:
+                raise la.LightningAttnError(st, "lightning_attn_fwd_traced")
+        else:
+            step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage = None
+    if traced:
+        names = ["tables", "summary", "scan", "fused"]
+        acc = [0.0] * 4
+        for e in evs:
+            for j in range(4):
+                acc[j] += hip.ms(e[j], e[j + 1])
+        stage = {n: acc[j] / steps for j, n in enumerate(names)}
+        stage["events_total"] = sum(hip.ms(e[0], e[4]) for e in evs) / steps
+        for e in evs:
+            hip.destroy(e)
+    chunk = la.lightning_attn_fwd_chunk_tokens(w.batch, w.heads, w.seq_len, w.head_dim,
+                                               w.block_size, 0, code)
+    del q, k, v, o, ws
+    torch.cuda.empty_cache()
+    return (t1 - t0) * 1000.0 / steps, stage, chunk, nbytes
+
+
+def bench_decode(w, reps, dev):
+    import torch
+    import linear_attention_attn_amd as la
+    import synth
+
+    S = synth.decode_state(w.batch, w.heads, w.head_dim, w.cid, dev)
+    ins = [synth.decode_step_inputs(w.batch, w.heads, w.head_dim, w.dtype, w.cid, t, dev)
+           for t in range(w.steps)]
+    o = torch.empty_like(ins[0][0])
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    code = la.LA_DTYPE_BF16 if w.dtype == "bf16" else la.LA_DTYPE_F32
+
+    def run_all():
+        for q, k, v in ins:
+            st = la.lightning_attn_decode(q, k, v, S, o, w.batch, w.heads, w.head_dim, code, stream)
+            if st != la.LA_OK:
+                raise la.LightningAttnError(st, "lightning_attn_decode")
+
+    run_all()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(reps):
+        a.record()
+        run_all()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / w.steps
+        best = ms if best is None else min(best, ms)
+    units = w.batch * w.heads
+    d = w.head_dim
+    bytes_step = units * (8 * d * d + 8 * d)   # fp32 state read+write; bf16 q, k, v, o
+    del S, ins, o
+    torch.cuda.empty_cache()
+    return best, bytes_step / (best * 1e-3) / 1e9, units / (best * 1e-3)
+
+
+def cpu_baseline(w, target_s):
+    """The oracle (recurrent form, fp64, OpenMP over units) on a bounded sample
+    of the prefill workload's (sequence, head) units; scaled to tokens/s."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    threads = min(16, len(os.sched_getaffinity(0)))
+    oracle.build(force=False)
+    n, d = w.seq_len, w.head_dim
+
+    def sample(nh):
+        q, k, v = synth.prefill_inputs(1, nh, n, d, w.dtype, w.cid, "cpu",
+                                       heads_subset=list(range(nh)))
+        return [x.to(torch.float32).numpy()[0] for x in (q, k, v)]
+
+    # probe with one unit per thread, then size the sample for ~target_s
+    nh = threads
+    q, k, v = sample(nh)
+    t0 = time.perf_counter()
+    oracle.causal_linear_attention(q, k, v, "recurrent", nthreads=threads)
+    dt = time.perf_counter() - t0
+    reps = max(1, min(w.heads // nh, int(target_s / max(dt, 1e-3))))
+    units = nh * reps
+    if reps > 1:
+        q, k, v = sample(units)
+        t0 = time.perf_counter()
+        oracle.causal_linear_attention(q, k, v, "recurrent", nthreads=threads)
+        dt = time.perf_counter() - t0
+    head_tokens = units * n
+    tok_s = head_tokens / w.heads / dt            # tokens carrying all heads
+    return {"value": tok_s, "unit": "tokens/s", "cores": min(threads, units), "kind": "oracle",
+            "sample": f"recurrent fp64 form on {units} of {w.batch * w.heads} (sequence, head) units "
+                      f"x {n} tokens, d={d} ({dt:.1f} s); tokens/s = head-tokens / {w.heads} heads / time",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extras", action="store_true", help="only the headline prefill workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--workload", default="minimax_layer")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads shard with no communication; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_attn_amd as la
+    import synth
+
+    la.load_library()
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    d, B = w.head_dim, w.block_size
+    head_tokens = w.batch * w.heads * w.seq_len
+    tokens = w.batch * w.seq_len
+
+    log(f"prefill {w.name}: {w.note}")
+    ms, stage, chunk, wsb = bench_prefill(w, args.steps, args.warmup, dev)
+    t = ms * 1e-3
+    flops = head_tokens * prefill_flops_per_head_token(d, B)
+    flops_dense = head_tokens * (4 * d * d + 4 * d * B)
+    alg_bytes = head_tokens * 4 * d * (2 if w.dtype == "bf16" else 4)
+    tflops = flops / t / 1e12
+    fused_ms = stage["fused"]
+    fused_gbs = alg_bytes / (fused_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": tokens / t,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic: q,k,v ~ N(0,1), q and k scaled by 1/sqrt(d), rounded to bf16",
+        "config": {"workload": f"{w.name} ({w.note})", "batch": w.batch, "heads": w.heads,
+                   "seq_len": w.seq_len, "head_dim": d, "block_size": B,
+                   "chunk_tokens": chunk, "parallelism": "single GPU"},
+        "tflops": tflops,
+        "mfma_frac": tflops / PEAK_BF16_TFLOPS,
+        "tflops_dense_executed": flops_dense / t / 1e12,
+        "hbm_gbs_step": alg_bytes / t / 1e9,
+        "roofline_frac_step": max(flops / (PEAK_BF16_TFLOPS * 1e12), alg_bytes / (PEAK_HBM_GBS * 1e9)) / t,
+        "kernels_ms": stage,
+        "workspace_bytes": wsb,
+        "roofline": {"bound": "hbm", "kernel": "k_fused (intra-block Q K^T, P V and Q S)",
+                     "achieved": fused_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": fused_gbs / PEAK_HBM_GBS, "traffic": None},
+    }
+    log(json.dumps({k: out[k] for k in ("value", "ms_per_step", "tflops", "kernels_ms")}))
+
+    if not args.no_extras:
+        wd = synth.WORKLOADS["decode256"]
+        log(f"decode {wd.name}: {wd.note}")
+        dms, dgbs, dtok = bench_decode(wd, 3, dev)
+        out["decode"] = {"workload": wd.note, "ms_per_step": dms, "gbs": dgbs,
+                         "hbm_frac": dgbs / PEAK_HBM_GBS, "head_steps_per_s": dtok}
+        log(json.dumps(out["decode"]))
+        wl = synth.WORKLOADS["long_1m"]
+        log(f"prefill {wl.name}: {wl.note}")
+        lms, lstage, lchunk, _ = bench_prefill(wl, 3, 1, dev)
+        lht = wl.batch * wl.heads * wl.seq_len
+        lbytes = lht * 4 * wl.head_dim * 2
+        out["long_1m"] = {"workload": wl.note, "ms_per_step": lms,
+                          "tokens_per_s": wl.seq_len / (lms * 1e-3),
+                          "tflops": lht * prefill_flops_per_head_token(wl.head_dim, wl.block_size)
+                          / (lms * 1e-3) / 1e12,
+                          "hbm_gbs": lbytes / (lms * 1e-3) / 1e9,
+                          "roofline_frac": lbytes / (PEAK_HBM_GBS * 1e9) / (lms * 1e-3),
+                          "kernels_ms": lstage, "chunk_tokens": lchunk}
+        out["long_1m"]["mfma_frac"] = out["long_1m"]["tflops"] / PEAK_BF16_TFLOPS
+        log(json.dumps(out["long_1m"]))
+
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        log(json.dumps(out["cpu_baseline"]))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

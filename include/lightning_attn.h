@@ -94,6 +94,26 @@ int lightning_attn_fwd(const void *q, const void *k, const void *v, void *o,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * lightning_attn_fwd with stage timing: identical work and results, and in
+ * addition records caller-created hipEvent_t handles (passed as void*) on
+ * `stream` at the stage boundaries, so a caller can time each kernel on the
+ * stream it runs on:
+ *   events[0] before the first launch,
+ *   events[1] after the chunk/offset tables,
+ *   events[2] after the per-chunk K^T V summaries,
+ *   events[3] after the exclusive scan of chunk states,
+ *   events[4] after the fused intra-block + Q S output kernel.
+ * nevents must be LA_FWD_NUM_EVENTS; a NULL events pointer or a NULL entry is
+ * LA_EINVAL.  The events are only recorded, never synchronised or destroyed.
+ */
+#define LA_FWD_NUM_EVENTS 5
+int lightning_attn_fwd_traced(const void *q, const void *k, const void *v, void *o,
+                              int batch, int heads, int64_t seq_len, int head_dim, int block_size,
+                              const int32_t *cu_seqlens, int dtype,
+                              void *workspace, size_t workspace_bytes, void *stream,
+                              void *const *events, int nevents);
+
+/*
  * One decode step for batch x heads independent sequences (wiki page section
  * "Lightning Attention 设计": inference only updates the d x d KV state,
  * O(d^2) per token; comparison table row "状态大小").

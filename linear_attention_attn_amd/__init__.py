@@ -21,12 +21,14 @@ __all__ = [
     "LA_DTYPE_BF16", "LA_DTYPE_F32", "LA_OK", "LA_EINVAL", "LA_EUNSUPPORTED", "LA_EWORKSPACE",
     "LA_EHIP", "LightningAttnError", "lib_path", "load_library",
     "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_chunk_tokens", "lightning_attn_fwd",
-    "lightning_attn_decode", "lightning_attn_strerror", "fwd", "decode",
+    "lightning_attn_fwd_traced", "lightning_attn_decode", "lightning_attn_strerror", "fwd",
+    "decode", "LA_FWD_NUM_EVENTS",
 ]
 
 LA_DTYPE_BF16 = 0
 LA_DTYPE_F32 = 1
 LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EWORKSPACE, LA_EHIP = 0, 1, 2, 3, 4
+LA_FWD_NUM_EVENTS = 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -58,6 +60,9 @@ def load_library():
     lib.lightning_attn_fwd_chunk_tokens.restype = i64
     lib.lightning_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, i32, vp, sz, vp]
     lib.lightning_attn_fwd.restype = i32
+    lib.lightning_attn_fwd_traced.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, i32, vp, sz,
+                                              vp, ctypes.POINTER(vp), i32]
+    lib.lightning_attn_fwd_traced.restype = i32
     lib.lightning_attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
     lib.lightning_attn_decode.restype = i32
     lib.lightning_attn_strerror.argtypes = [i32]
@@ -92,6 +97,14 @@ def lightning_attn_fwd(q, k, v, o, batch, heads, seq_len, head_dim, block_size, 
     return int(load_library().lightning_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, heads, seq_len, head_dim, block_size,
         _ptr(cu_seqlens), dtype, _ptr(workspace), workspace_bytes, stream))
+
+
+def lightning_attn_fwd_traced(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens,
+                              dtype, workspace, workspace_bytes, stream, events, nevents) -> int:
+    arr = (ctypes.c_void_p * max(1, len(events)))(*events) if events is not None else None
+    return int(load_library().lightning_attn_fwd_traced(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, heads, seq_len, head_dim, block_size,
+        _ptr(cu_seqlens), dtype, _ptr(workspace), workspace_bytes, stream, arr, nevents))
 
 
 def lightning_attn_decode(q, k, v, state, o, batch, heads, head_dim, dtype, stream) -> int:

@@ -105,9 +105,10 @@ int64_t lightning_attn_fwd_chunk_tokens(int batch, int heads, int64_t seq_len, i
     return p.chunk;
 }
 
-int lightning_attn_fwd(const void *q, const void *k, const void *v, void *o, int batch, int heads,
-                       int64_t seq_len, int head_dim, int block_size, const int32_t *cu_seqlens,
-                       int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+static int fwd_common(const void *q, const void *k, const void *v, void *o, int batch, int heads,
+                      int64_t seq_len, int head_dim, int block_size, const int32_t *cu_seqlens,
+                      int dtype, void *workspace, size_t workspace_bytes, void *stream,
+                      void *const *events) {
     int st = la::check_fwd_shape(batch, heads, seq_len, head_dim, block_size, dtype);
     if (st != LA_OK) return st;
     if (seq_len == 0) return LA_OK;
@@ -120,7 +121,26 @@ int lightning_attn_fwd(const void *q, const void *k, const void *v, void *o, int
     if (!workspace || workspace_bytes < a.plan.bytes) return LA_EWORKSPACE;
     if (((uintptr_t)workspace & 255) != 0) return LA_EINVAL;
     a.workspace = static_cast<char *>(workspace);
-    return la::launch_fwd(a, stream) == 0 ? LA_OK : LA_EHIP;
+    return la::launch_fwd(a, stream, events) == 0 ? LA_OK : LA_EHIP;
+}
+
+int lightning_attn_fwd(const void *q, const void *k, const void *v, void *o, int batch, int heads,
+                       int64_t seq_len, int head_dim, int block_size, const int32_t *cu_seqlens,
+                       int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    return fwd_common(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens, dtype,
+                      workspace, workspace_bytes, stream, nullptr);
+}
+
+int lightning_attn_fwd_traced(const void *q, const void *k, const void *v, void *o, int batch,
+                              int heads, int64_t seq_len, int head_dim, int block_size,
+                              const int32_t *cu_seqlens, int dtype, void *workspace,
+                              size_t workspace_bytes, void *stream, void *const *events,
+                              int nevents) {
+    if (!events || nevents != LA_FWD_NUM_EVENTS) return LA_EINVAL;
+    for (int i = 0; i < nevents; ++i)
+        if (!events[i]) return LA_EINVAL;
+    return fwd_common(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens, dtype,
+                      workspace, workspace_bytes, stream, events);
 }
 
 int lightning_attn_decode(const void *q, const void *k, const void *v, float *state, void *o, int batch,

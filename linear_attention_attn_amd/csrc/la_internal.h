@@ -43,9 +43,10 @@ struct FwdArgs {
     FwdPlan plan;
 };
 
-// Queue the forward kernels on `stream` (a hipStream_t).  Returns 0 or a HIP
-// error code.
-int launch_fwd(const FwdArgs &a, void *stream);
+// Queue the forward kernels on `stream` (a hipStream_t).  When `events` is
+// non-null it holds 5 hipEvent_t handles recorded at the stage boundaries.
+// Returns 0 or a HIP error code.
+int launch_fwd(const FwdArgs &a, void *stream, void *const *events);
 
 // Queue one decode step.  Returns 0 or a HIP error code.
 int launch_decode(const void *q, const void *k, const void *v, float *state, void *o,

@@ -538,10 +538,16 @@ __global__ __launch_bounds__(512, 1) void k_fused(KParams p) {
 // -------------------------------------------------------------- host side
 
 template <typename T, int D, int BLK>
-static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream_t st) {
+static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream_t st, void *const *ev) {
+    auto mark = [&](int i) {
+        if (ev) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), st);
+    };
     const dim3 gchunks((unsigned)plan.nchunk_ub, (unsigned)kp.heads);
+    mark(0);
     hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, st, kp);
+    mark(1);
     hipLaunchKernelGGL((k_summary<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
+    mark(2);
     const dim3 gtiles((unsigned)plan.ntile_ub, (D * D) / kScanThreads, (unsigned)kp.heads);
     if (plan.scan_tiles) {
         hipLaunchKernelGGL(k_scan_reduce<D>, gtiles, dim3(kScanThreads), 0, st, kp);
@@ -549,20 +555,23 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
                            dim3(kScanThreads), 0, st, kp);
     }
     hipLaunchKernelGGL(k_scan_apply<D>, gtiles, dim3(kScanThreads), 0, st, kp, plan.scan_tiles ? 1 : 0);
+    mark(3);
     hipLaunchKernelGGL((k_fused<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
+    mark(4);
     return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_blk(const KParams &kp, const FwdPlan &plan, int blk, hipStream_t st) {
+static hipError_t launch_blk(const KParams &kp, const FwdPlan &plan, int blk, hipStream_t st,
+                             void *const *ev) {
     switch (blk) {
-        case 64: return launch_typed<T, D, 64>(kp, plan, st);
-        case 128: return launch_typed<T, D, 128>(kp, plan, st);
-        default: return launch_typed<T, D, 256>(kp, plan, st);
+        case 64: return launch_typed<T, D, 64>(kp, plan, st, ev);
+        case 128: return launch_typed<T, D, 128>(kp, plan, st, ev);
+        default: return launch_typed<T, D, 256>(kp, plan, st, ev);
     }
 }
 
-int launch_fwd(const FwdArgs &a, void *stream) {
+int launch_fwd(const FwdArgs &a, void *stream, void *const *events) {
     KParams kp;
     kp.q = a.q; kp.k = a.k; kp.v = a.v; kp.o = a.o;
     kp.cu = a.cu_seqlens;
@@ -580,11 +589,11 @@ int launch_fwd(const FwdArgs &a, void *stream) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (a.dtype == 0) {
-        e = a.head_dim == 64 ? launch_blk<bf16_t, 64>(kp, a.plan, a.block_size, st)
-                             : launch_blk<bf16_t, 128>(kp, a.plan, a.block_size, st);
+        e = a.head_dim == 64 ? launch_blk<bf16_t, 64>(kp, a.plan, a.block_size, st, events)
+                             : launch_blk<bf16_t, 128>(kp, a.plan, a.block_size, st, events);
     } else {
-        e = a.head_dim == 64 ? launch_blk<float, 64>(kp, a.plan, a.block_size, st)
-                             : launch_blk<float, 128>(kp, a.plan, a.block_size, st);
+        e = a.head_dim == 64 ? launch_blk<float, 64>(kp, a.plan, a.block_size, st, events)
+                             : launch_blk<float, 128>(kp, a.plan, a.block_size, st, events);
     }
     return (int)e;
 }
