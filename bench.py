@@ -162,6 +162,28 @@ def bench_decode(w, reps, dev):
     return best, bytes_step / (best * 1e-3) / 1e9, units / (best * 1e-3)
 
 
+def copy_calibration(dev, nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size (reads nbytes, writes nbytes)."""
+    import torch
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for _ in range(reps):
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": best,
+            "gbs_read_plus_write": 2 * nbytes / (best * 1e-3) / 1e9}
+
+
 def cpu_baseline(w, target_s):
     """The oracle (recurrent form, fp64, OpenMP over units) on a bounded sample
     of the prefill workload's (sequence, head) units; scaled to tokens/s."""
@@ -210,6 +232,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--workload", default="minimax_layer")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also time a plain 1 GiB device copy (the reference kernel for the "
+                         "HBM byte counters) and report its GB/s")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -287,6 +312,10 @@ def main():
                           "kernels_ms": lstage, "chunk_tokens": lchunk}
         out["long_1m"]["mfma_frac"] = out["long_1m"]["tflops"] / PEAK_BF16_TFLOPS
         log(json.dumps(out["long_1m"]))
+
+    if args.copy_calibration:
+        out["copy_calibration"] = copy_calibration(dev)
+        log(json.dumps(out["copy_calibration"]))
 
     if not args.no_cpu:
         log("cpu baseline (oracle)")

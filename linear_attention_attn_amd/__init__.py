@@ -41,7 +41,8 @@ class LightningAttnError(RuntimeError):
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "liblightning_attn.so")
+    """The in-tree library, or the file LIGHTNING_ATTN_LIB names."""
+    return os.environ.get("LIGHTNING_ATTN_LIB") or os.path.join(_HERE, "liblightning_attn.so")
 
 
 def load_library():

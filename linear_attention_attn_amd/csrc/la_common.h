@@ -52,17 +52,17 @@ __device__ __forceinline__ void mma(f32x4_t &acc, const Frag<float> &a, const Fr
     for (int m = 0; m < 8; ++m) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.f[m], b.f[m], acc, 0, 0, 0);
 }
 
-// ---- fp32 -> bf16, round to nearest even (NaN kept quiet) ---------------
+// ---- fp32 -> bf16, round to nearest even --------------------------------
+// gfx950 converts two floats to packed bf16 in one instruction
+// (v_cvt_pk_bf16_f32, rounding to nearest even in the default mode).
 
-__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return bf16_bits_rne(lo) | (bf16_bits_rne(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x) { return pack_bf16x2(x, 0.f) & 0xffffu; }
 
 // Build an operand fragment from eight fp32 values (used for the masked
 // score tile that feeds the P V product).
@@ -166,6 +166,78 @@ __device__ __forceinline__ void lds_write4(char *base, uint32_t row, uint32_t e0
     } else {
         *reinterpret_cast<f32x4_t *>(base + R::off(row, e0 * 4)) = x;
     }
+}
+
+// ---- LDS transpose reads and global -> LDS DMA (gfx950) ------------------
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lanes 4r..4r+3 each name a
+// run of four 16-bit elements; together they form row r of a 4 x 16 matrix
+// X.  Lane i of the group receives column i: X[0][i], X[1][i], X[2][i],
+// X[3][i].  With lane 4r+q pointing at element 4q of row r of a 16-column
+// window, lane i gets the window's column i from four rows: a token-strided
+// MFMA operand read from a token-major (row-major) tile.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const char *p) {
+    v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)(p));
+    return __builtin_bit_cast(u32x2_t, r);
+}
+
+// 16 bytes from global memory to LDS for every lane of the wave: lane l's
+// bytes land at lds + 16 * l (lds must be wave-uniform).  No VGPR holds the
+// data and the load counts in vmcnt like any vector-memory load.
+//
+// Issued from inline assembly on purpose: the compiler then does not track
+// the LDS write, so it does not make every later LDS read wait for all
+// outstanding DMA (the callers wait for exactly the stage they read with
+// wait_vm_lgkm0 + wg_barrier).  The compiler also does not count these loads
+// in its own vmcnt bookkeeping for register loads; that only makes its waits
+// stricter than needed, never looser, since the hardware count is larger.
+__device__ __forceinline__ void dma16(const void *g, const char *lds) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)lds;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(m0)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4 left at its maximum, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+// Runtime count (wave-uniform) mapped onto the immediate forms.
+__device__ __forceinline__ void wait_vm_lgkm0(int n) {
+    switch (n) {
+#define LA_WAIT_CASE(k) case k: wait_vm_lgkm0<k>(); break;
+        LA_WAIT_CASE(0) LA_WAIT_CASE(1) LA_WAIT_CASE(2) LA_WAIT_CASE(3) LA_WAIT_CASE(4)
+        LA_WAIT_CASE(5) LA_WAIT_CASE(6) LA_WAIT_CASE(7) LA_WAIT_CASE(8) LA_WAIT_CASE(9)
+        LA_WAIT_CASE(10) LA_WAIT_CASE(11) LA_WAIT_CASE(12) LA_WAIT_CASE(13) LA_WAIT_CASE(14)
+        LA_WAIT_CASE(15) LA_WAIT_CASE(16) LA_WAIT_CASE(17) LA_WAIT_CASE(18) LA_WAIT_CASE(19)
+        LA_WAIT_CASE(20) LA_WAIT_CASE(21) LA_WAIT_CASE(22) LA_WAIT_CASE(23) LA_WAIT_CASE(24)
+        LA_WAIT_CASE(25) LA_WAIT_CASE(26) LA_WAIT_CASE(27) LA_WAIT_CASE(28) LA_WAIT_CASE(29)
+        LA_WAIT_CASE(30) LA_WAIT_CASE(31) LA_WAIT_CASE(32) LA_WAIT_CASE(33) LA_WAIT_CASE(34)
+        LA_WAIT_CASE(35) LA_WAIT_CASE(36) LA_WAIT_CASE(37) LA_WAIT_CASE(38) LA_WAIT_CASE(39)
+        LA_WAIT_CASE(40) LA_WAIT_CASE(41) LA_WAIT_CASE(42) LA_WAIT_CASE(43) LA_WAIT_CASE(44)
+        LA_WAIT_CASE(45) LA_WAIT_CASE(46) LA_WAIT_CASE(47) LA_WAIT_CASE(48) LA_WAIT_CASE(49)
+        LA_WAIT_CASE(50) LA_WAIT_CASE(51) LA_WAIT_CASE(52) LA_WAIT_CASE(53) LA_WAIT_CASE(54)
+        LA_WAIT_CASE(55) LA_WAIT_CASE(56) LA_WAIT_CASE(57) LA_WAIT_CASE(58) LA_WAIT_CASE(59)
+        LA_WAIT_CASE(60) LA_WAIT_CASE(61) LA_WAIT_CASE(62) LA_WAIT_CASE(63)
+#undef LA_WAIT_CASE
+        default: wait_vm_lgkm0<0>(); break;
+    }
+}
+
+// Workgroup barrier with no implied memory wait: the caller has already
+// waited for exactly what the next phase reads.  The empty asm statements keep
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void wg_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }

@@ -35,6 +35,8 @@ struct KParams {
     int32_t *tile_off;      // [nseq + 1]
     float *states;          // [heads][nchunk_ub][D*D]
     float *tilesum;         // [heads][ntile_ub][D*D]
+    uint32_t *zero;         // kZeroBytes of zeros (rows past a sequence end are loaded from here)
+    uint32_t *sink;         // kSinkBytes: target of the stores of rows past a sequence end
     int64_t seq_len;        // dense: per sequence; packed: total tokens
     int64_t chunk;          // tokens per chunk
     int64_t nchunk_ub, ntile_ub;
@@ -75,6 +77,8 @@ __device__ __forceinline__ int find_seg(const int32_t *off, int n, int64_t x) {
 // -------------------------------------------------------------- k_prep
 // chunk_off[s] = sum_{s' < s} ceil(L_s' / C);  tile_off[s] = sum ceil(nc_s' / G).
 constexpr int kPrepThreads = 1024;
+constexpr int kZeroBytes = 512;
+constexpr int kSinkBytes = 512;
 
 __global__ __launch_bounds__(kPrepThreads) void k_prep(KParams p) {
     __shared__ int64_t sc[kPrepThreads], st[kPrepThreads];
@@ -89,6 +93,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(KParams p) {
         g += (nc + p.group - 1) / p.group;
     }
     sc[t] = c; st[t] = g;
+    if (t < kZeroBytes / 4) p.zero[t] = 0u;
     __syncthreads();
     for (int d = 1; d < kPrepThreads; d <<= 1) {   // inclusive Hillis-Steele scan
         int64_t a = t >= d ? sc[t - d] : 0, b = t >= d ? st[t - d] : 0;
@@ -535,6 +540,332 @@ __global__ __launch_bounds__(512, 1) void k_fused(KParams p) {
     }
 }
 
+// ================================================================ bf16 path
+// K and V tiles are copied global -> LDS by the DMA engine (no VGPR staging)
+// into a ring of stages, token-major with a 16-byte-chunk swizzle.  Operands
+// that reduce over d (Q K^T) read rows with ds_read_b128; operands that reduce
+// over tokens (P V, K^T V) read columns with ds_read_b64_tr_b16.  Rows past a
+// sequence end are loaded from a zero area, so they add nothing.
+
+template <int D, int TJ>
+struct DmaTile {
+    static constexpr int RB = D * 2;                 // bytes per token row
+    static constexpr int TB = TJ * RB;               // bytes per tensor tile
+    static constexpr int SB = 2 * TB;                // K then V
+    static constexpr int NI = TB / 1024;             // 1 KiB wave instructions per tensor
+    static constexpr int IPW = 2 * NI / 8;           // per wave (8 waves)
+    static_assert(TB % 1024 == 0 && (2 * NI) % 8 == 0, "tile split");
+
+    // Queue the K and V rows [tok0, tok0 + TJ) of a unit into `stage`.
+    __device__ __forceinline__ static void issue(char *stage, const bf16_t *kb, const bf16_t *vb,
+                                                 int64_t tok0, int64_t tend, const bf16_t *zero) {
+        using R = LdsRows<RB>;
+        const int w = wave_id(), l = lane_id();
+#pragma unroll
+        for (int ii = 0; ii < IPW; ++ii) {
+            const int gi = w * IPW + ii;
+            const bool isv = gi >= NI;
+            const int x = isv ? gi - NI : gi;
+            const uint32_t byte = (uint32_t)x * 1024u + (uint32_t)l * 16u;
+            const uint32_t row = byte / RB;
+            const uint32_t lch = ((byte % RB) >> 4) ^ R::swz(row);
+            const int64_t tok = tok0 + row;
+            const bf16_t *src = tok < tend ? (isv ? vb : kb) + tok * D + lch * 8 : zero + lch * 8;
+            dma16(src, stage + (isv ? TB : 0) + x * 1024);
+        }
+    }
+};
+
+// Eight token-strided values of column `col` for MFMA k-slots: slots 0..3 are
+// tokens jb + 4g + (0..3), slots 4..7 tokens jb + 16 + 4g + (0..3) (g = lane/16);
+// the lane's column is col0 + lane % 16.
+template <int RB>
+__device__ __forceinline__ Frag<bf16_t> lds_cols8(const char *tile, int jb, int col0) {
+    using R = LdsRows<RB>;
+    const int l = lane_id(), g = l >> 4, r = (l >> 2) & 3, q = l & 3;
+    const uint32_t b = (uint32_t)(col0 + 4 * q) * 2u;
+    const u32x2_t a0 = lds_read_tr16(tile + R::off(jb + 4 * g + r, b));
+    const u32x2_t a1 = lds_read_tr16(tile + R::off(jb + 16 + 4 * g + r, b));
+    Frag<bf16_t> f;
+    f.u = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
+    return f;
+}
+
+// S[ia][ib] += K^T V over one token-major tile of TJ tokens.
+template <int D, int TJ, int SA, int SB>
+__device__ __forceinline__ void state_update_tr(f32x4_t (&S)[SA][SB], const char *kt, const char *vt,
+                                                int a0, int b0) {
+    constexpr int RB = D * 2;
+#pragma unroll
+    for (int jg = 0; jg < TJ / 32; ++jg) {
+        Frag<bf16_t> A[SA], B[SB];
+#pragma unroll
+        for (int ia = 0; ia < SA; ++ia) A[ia] = lds_cols8<RB>(kt, jg * 32, (a0 + ia) * 16);
+#pragma unroll
+        for (int ib = 0; ib < SB; ++ib) B[ib] = lds_cols8<RB>(vt, jg * 32, (b0 + ib) * 16);
+#pragma unroll
+        for (int ia = 0; ia < SA; ++ia)
+#pragma unroll
+            for (int ib = 0; ib < SB; ++ib) mma(S[ia][ib], A[ia], B[ib]);
+    }
+}
+
+// U_c = K_c^T V_c with a two-stage DMA ring (two workgroups fit per CU).
+template <int D, int BLK>
+__global__ __launch_bounds__(512, 2) void k_summary_dma(KParams p) {
+    using C = Cfg<bf16_t, D, BLK>;
+    using DT = DmaTile<D, C::TJ>;
+    __shared__ __attribute__((aligned(16))) char lds[2 * DT::SB];
+    const int h = blockIdx.y;
+    const int64_t gch = blockIdx.x;
+    if (gch >= p.chunk_off[p.nseq]) return;
+    const int s = find_seg(p.chunk_off, p.nseq, gch);
+    const Unit u = unit_of<D>(p, s, h);
+    const int64_t t0 = (gch - p.chunk_off[s]) * p.chunk;
+    const int64_t t1 = min(u.len, t0 + p.chunk);
+    const bf16_t *kb = reinterpret_cast<const bf16_t *>(p.k) + u.base;
+    const bf16_t *vb = reinterpret_cast<const bf16_t *>(p.v) + u.base;
+    const bf16_t *zero = reinterpret_cast<const bf16_t *>(p.zero);
+
+    const int w = wave_id(), l = lane_id(), c = l & 15, g = l >> 4;
+    const int a0 = C::SA * (w % C::AW), b0 = C::SB * (w / C::AW);
+    f32x4_t S[C::SA][C::SB];
+#pragma unroll
+    for (int ia = 0; ia < C::SA; ++ia)
+#pragma unroll
+        for (int ib = 0; ib < C::SB; ++ib) S[ia][ib] = zero4();
+
+    const int64_t ntile = (t1 - t0 + C::TJ - 1) / C::TJ;
+    DT::issue(lds, kb, vb, t0, t1, zero);
+    for (int64_t it = 0; it < ntile; ++it) {
+        char *cur = lds + (it & 1) * DT::SB;
+        if (it + 1 < ntile) {
+            DT::issue(lds + ((it + 1) & 1) * DT::SB, kb, vb, t0 + (it + 1) * C::TJ, t1, zero);
+            wait_vm_lgkm0<DT::IPW>();
+        } else {
+            wait_vm_lgkm0<0>();
+        }
+        wg_barrier();
+        state_update_tr<D, C::TJ, C::SA, C::SB>(S, cur, cur + DT::TB, a0, b0);
+        wait_vm_lgkm0<DT::IPW>();   // own LDS reads done (the DMA in flight may stay)
+        wg_barrier();               // nobody reads `cur` any more: it may be refilled
+    }
+    float *dst = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
+#pragma unroll
+    for (int ia = 0; ia < C::SA; ++ia)
+#pragma unroll
+        for (int ib = 0; ib < C::SB; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dst[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c] = S[ia][ib][r];
+}
+
+// Per chunk: walk the blocks carrying S; per block O^T = S^T Q^T + V^T P^T
+// with P = mask(Q K^T), then S += K^T V.  K/V tiles stream through a 3-stage
+// DMA ring (prefetch distance 2).  Every vector-memory instruction a wave
+// issues is unconditional, so the wait before each barrier can name exactly
+// how many younger operations may still be in flight.
+template <int D, int BLK>
+__global__ __launch_bounds__(512, 1) void k_fused_dma(KParams p) {
+    using T = bf16_t;
+    using C = Cfg<T, D, BLK>;
+    using DT = DmaTile<D, C::TJ>;
+    constexpr int NST = 3;
+    constexpr int TPB = BLK / C::TJ;                 // tiles per block
+    constexpr int QL = C::NSW * C::KC;               // Q loads per wave per block
+    constexpr int OS = C::NSW * C::NCT;              // O stores per wave per block
+    __shared__ __attribute__((aligned(16))) char lds[NST * DT::SB + C::ST_BYTES];
+    char *const st = lds + NST * DT::SB;
+
+    const int h = blockIdx.y;
+    const int64_t gch = blockIdx.x;
+    if (gch >= p.chunk_off[p.nseq]) return;
+    const int s = find_seg(p.chunk_off, p.nseq, gch);
+    const Unit u = unit_of<D>(p, s, h);
+    const int64_t cl = gch - p.chunk_off[s];
+    const int64_t t0 = cl * p.chunk;
+    const int64_t t1 = min(u.len, t0 + p.chunk);
+    const T *qb = reinterpret_cast<const T *>(p.q) + u.base;
+    const T *kb = reinterpret_cast<const T *>(p.k) + u.base;
+    const T *vb = reinterpret_cast<const T *>(p.v) + u.base;
+    T *ob = reinterpret_cast<T *>(p.o) + u.base;
+    const T *zero = reinterpret_cast<const T *>(p.zero);
+    T *sink = reinterpret_cast<T *>(p.sink);
+
+    const int w = wave_id(), l = lane_id(), c = l & 15, g = l >> 4;
+    const int a0 = C::SA * (w % C::AW), b0 = C::SB * (w / C::AW);
+    const int ct0 = C::CSPLIT == 1 ? 0 : (w >> 2) * C::NCT;
+    const int64_t ntile = (t1 - t0 + C::TJ - 1) / C::TJ;
+    const int64_t nblk = (t1 - t0 + BLK - 1) / BLK;
+
+    // ---- state at the chunk start (exclusive prefix from the scan)
+    f32x4_t S[C::SA][C::SB];
+    {
+        const float *src = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
+        const bool first = cl == 0;
+#pragma unroll
+        for (int ia = 0; ia < C::SA; ++ia)
+#pragma unroll
+            for (int ib = 0; ib < C::SB; ++ib)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    S[ia][ib][r] = first ? 0.f : src[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c];
+#pragma unroll
+        for (int ia = 0; ia < C::SA; ++ia)
+#pragma unroll
+            for (int ib = 0; ib < C::SB; ++ib)
+                lds_write4<T, C::ST_ROW>(st, (b0 + ib) * 16 + c, (a0 + ia) * 16 + 4 * g, S[ia][ib]);
+    }
+
+    // Q fragments of this wave's row slabs (rows past the end re-read the last
+    // row: their outputs are never stored and each query row only feeds its
+    // own output row)
+    Frag<T> Q[C::NSW][C::KC];
+    auto load_q = [&](int64_t tb) {
+#pragma unroll
+        for (int si = 0; si < C::NSW; ++si) {
+            const int64_t row = min(tb + 16 * slab_of<BLK>(w, si) + c, t1 - 1);
+#pragma unroll
+            for (int kc = 0; kc < C::KC; ++kc)
+                Q[si][kc].u = *reinterpret_cast<const u32x4_t *>(qb + row * D + kc * 32 + 8 * g);
+        }
+    };
+    load_q(t0);
+    DT::issue(lds, kb, vb, t0, t1, zero);
+    wait_vm_lgkm0<0>();              // Q, the start state and tile 0 are in
+    if (ntile > 1) DT::issue(lds + DT::SB, kb, vb, t0 + C::TJ, t1, zero);
+    wg_barrier();
+
+    f32x4_t O[C::NSW][C::NCT];
+    for (int64_t t = 0; t < ntile; ++t) {
+        const int jt = (int)(t % TPB);
+        const int64_t bi = t / TPB;
+        const int64_t tb = t0 + bi * BLK;
+        const bool first = jt == 0;
+        const bool last = jt == TPB - 1 || t == ntile - 1;
+        const bool more = bi + 1 < nblk;
+        const bool dma = t + 2 < ntile;
+        if (dma) DT::issue(lds + ((t + 2) % NST) * DT::SB, kb, vb, t0 + (t + 2) * C::TJ, t1, zero);
+        const char *kr = lds + (t % NST) * DT::SB;
+        const char *vr = kr + DT::TB;
+
+        if (first) {
+            // ---- inter-block right product with the block-start state
+#pragma unroll
+            for (int si = 0; si < C::NSW; ++si)
+#pragma unroll
+                for (int ct = 0; ct < C::NCT; ++ct) O[si][ct] = zero4();
+#pragma unroll
+            for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+                for (int kc = 0; kc < C::KC; ++kc) {
+                    const Frag<T> A = lds_read8<T, C::ST_ROW>(st, (ct0 + ct) * 16 + c, kc * 32 + 8 * g);
+#pragma unroll
+                    for (int si = 0; si < C::NSW; ++si) mma(O[si][ct], A, Q[si][kc]);
+                }
+        }
+
+        // ---- intra-block left product for this K/V tile
+#pragma unroll
+        for (int jg = 0; jg < C::TJ / 32; ++jg) {
+            const int jb = jt * C::TJ + jg * 32;          // block-local first token of the group
+            f32x4_t P[C::NSW][2];
+            bool need[C::NSW], need1[C::NSW];
+#pragma unroll
+            for (int si = 0; si < C::NSW; ++si) {
+                const int i0 = 16 * slab_of<BLK>(w, si);
+                need[si] = jb <= i0 + 15;
+                need1[si] = jb + 16 <= i0 + 15;
+                P[si][0] = zero4();
+                P[si][1] = zero4();
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                bool any = false;
+#pragma unroll
+                for (int si = 0; si < C::NSW; ++si) any |= hh ? need1[si] : need[si];
+                if (!any) continue;
+#pragma unroll
+                for (int kc = 0; kc < C::KC; ++kc) {
+                    const Frag<T> A = lds_read8<T, DT::RB>(kr, jg * 32 + 16 * hh + c, kc * 32 + 8 * g);
+#pragma unroll
+                    for (int si = 0; si < C::NSW; ++si)
+                        if (hh ? need1[si] : need[si]) mma(P[si][hh], A, Q[si][kc]);
+                }
+            }
+            Frag<T> PF[C::NSW];
+#pragma unroll
+            for (int si = 0; si < C::NSW; ++si) {
+                const int i0 = 16 * slab_of<BLK>(w, si);
+                const int i = i0 + c;
+                if (need[si] && jb + 31 > i0) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (jb + 4 * g + r > i) P[si][0][r] = 0.f;
+                        if (jb + 16 + 4 * g + r > i) P[si][1][r] = 0.f;
+                    }
+                }
+                PF[si] = frag_from_f32(P[si][0], P[si][1], T{});
+            }
+            bool anyg = false;
+#pragma unroll
+            for (int si = 0; si < C::NSW; ++si) anyg |= need[si];
+            if (anyg) {
+#pragma unroll
+                for (int ct = 0; ct < C::NCT; ++ct) {
+                    const Frag<T> A = lds_cols8<DT::RB>(vr, jg * 32, (ct0 + ct) * 16);
+#pragma unroll
+                    for (int si = 0; si < C::NSW; ++si)
+                        if (need[si]) mma(O[si][ct], A, PF[si]);
+                }
+            }
+        }
+        // ---- store O: lane holds row (16*slab + c), columns 16*ct + 4g .. +3
+        auto store_o = [&]() {
+#pragma unroll
+            for (int si = 0; si < C::NSW; ++si) {
+                const int64_t row = tb + 16 * slab_of<BLK>(w, si) + c;
+                const bool ok = row < t1;
+#pragma unroll
+                for (int ct = 0; ct < C::NCT; ++ct)
+                    store4(ok ? ob + row * D + (ct0 + ct) * 16 + 4 * g : sink + 4 * l, O[si][ct]);
+            }
+        };
+        auto write_state = [&]() {
+            if (first) {                     // one-tile blocks: the state copy was read this iteration
+                wait_vm_lgkm0<63>();
+                wg_barrier();
+            }
+#pragma unroll
+            for (int ia = 0; ia < C::SA; ++ia)
+#pragma unroll
+                for (int ib = 0; ib < C::SB; ++ib)
+                    lds_write4<T, C::ST_ROW>(st, (b0 + ib) * 16 + c, (a0 + ia) * 16 + 4 * g, S[ia][ib]);
+        };
+        if (last && more) load_q(tb + BLK);
+        if (more) state_update_tr<D, C::TJ, C::SA, C::SB>(S, kr, vr, a0, b0);
+        if (last) {
+            store_o();
+            if (more) write_state();
+        }
+        if (t + 1 < ntile) {
+            // Tile t+1's DMA was issued before: at the top of iteration t-1 (or in
+            // the prologue).  Younger vector-memory operations that may stay in
+            // flight: the Q loads and O stores of iteration t-1 (if it ended a
+            // block), this iteration's DMA, and its Q loads and O stores.
+            int n = dma ? DT::IPW : 0;
+            if (last) n += OS + (more ? QL : 0);
+            if (t > 0) {
+                const int64_t tp = t - 1;
+                const bool lastp = (int)(tp % TPB) == TPB - 1;
+                if (lastp) n += OS + QL;     // a block ended at t-1 and block bi followed it
+            }
+            wait_vm_lgkm0(n);
+            wg_barrier();
+        }
+    }
+}
+
 // -------------------------------------------------------------- host side
 
 template <typename T, int D, int BLK>
@@ -546,7 +877,10 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
     mark(0);
     hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, st, kp);
     mark(1);
-    hipLaunchKernelGGL((k_summary<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
+    if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL((k_summary_dma<D, BLK>), gchunks, dim3(512), 0, st, kp);
+    else
+        hipLaunchKernelGGL((k_summary<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
     mark(2);
     const dim3 gtiles((unsigned)plan.ntile_ub, (D * D) / kScanThreads, (unsigned)kp.heads);
     if (plan.scan_tiles) {
@@ -556,7 +890,10 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
     }
     hipLaunchKernelGGL(k_scan_apply<D>, gtiles, dim3(kScanThreads), 0, st, kp, plan.scan_tiles ? 1 : 0);
     mark(3);
-    hipLaunchKernelGGL((k_fused<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
+    if constexpr (sizeof(T) == 2)
+        hipLaunchKernelGGL((k_fused_dma<D, BLK>), gchunks, dim3(512), 0, st, kp);
+    else
+        hipLaunchKernelGGL((k_fused<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
     mark(4);
     return hipGetLastError();
 }
@@ -579,6 +916,8 @@ int launch_fwd(const FwdArgs &a, void *stream, void *const *events) {
     kp.tile_off = reinterpret_cast<int32_t *>(a.workspace + a.plan.off_tile_off);
     kp.states = reinterpret_cast<float *>(a.workspace + a.plan.off_states);
     kp.tilesum = reinterpret_cast<float *>(a.workspace + a.plan.off_tilesum);
+    kp.zero = reinterpret_cast<uint32_t *>(a.workspace + a.plan.off_zero);
+    kp.sink = reinterpret_cast<uint32_t *>(a.workspace + a.plan.off_sink);
     kp.seq_len = a.seq_len;
     kp.chunk = a.plan.chunk;
     kp.nchunk_ub = a.plan.nchunk_ub;
