@@ -36,22 +36,29 @@ static int64_t env_i64(const char *name, int64_t dflt) {
     return (end && *end == 0 && v > 0) ? (int64_t)v : dflt;
 }
 
-// Chunk length: the largest power-of-two multiple of the block size (up to
-// 8192 tokens, and not beyond the average sequence) that still leaves about
-// kTargetGroups workgroups, so the chip fills while the per-chunk state
-// traffic (64 KiB of fp32 at d = 128, several times per chunk) stays small
-// against the 4 * d * 2 bytes per token of q, k, v and o.  LA_CHUNK_TOKENS
+// Chunk length C (tokens one workgroup walks carrying the state; a multiple
+// of the block size).  The work is W = units * average length head-tokens
+// over kCUs compute units.  When W / kCUs covers a whole sequence, every
+// sequence is one chunk: no chunk summary or scan is needed at all.
+// Otherwise C is the largest power of two <= W / kCUs (so there are at least
+// about kCUs chunks), at most kMaxChunk: the per-chunk state traffic (a d x d
+// fp32 state written, scanned and read once per chunk) is then a few percent
+// of the 4 * d * 2 bytes per token of q, k, v and o.  LA_CHUNK_TOKENS
 // overrides it (rounded down to a multiple of the block size).
 void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int block_size, bool varlen,
                    FwdPlan *plan) {
-    const int64_t kTargetGroups = env_i64("LA_TARGET_GROUPS", 2048);
-    const int64_t kMaxChunk = 8192;
+    const int64_t kCUs = env_i64("LA_TARGET_GROUPS", 256);
+    const int64_t kMaxChunk = 16384;
     const int64_t units = (int64_t)batch * heads;
     const int64_t lavg = std::max<int64_t>(1, varlen ? seq_len / batch : seq_len);
-    int64_t C = block_size;
-    while (C * 2 <= kMaxChunk && C < lavg &&
-           units * ((lavg + 2 * C - 1) / (2 * C)) >= kTargetGroups)
-        C *= 2;
+    const int64_t per_cu = std::max<int64_t>(1, units * lavg / kCUs);
+    int64_t C;
+    if (!varlen && per_cu >= seq_len) {
+        C = (seq_len + block_size - 1) / block_size * block_size;   // one chunk per sequence
+    } else {
+        C = block_size;
+        while (C * 2 <= kMaxChunk && C * 2 <= per_cu) C *= 2;
+    }
     const int64_t forced = env_i64("LA_CHUNK_TOKENS", 0);
     if (forced > 0) C = std::max<int64_t>(block_size, forced / block_size * block_size);
 
@@ -64,6 +71,7 @@ void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int bloc
         p.nchunk_ub = (int64_t)batch * cps;
         p.ntile_ub = (int64_t)batch * ((cps + G - 1) / G);
         p.scan_tiles = cps > G;
+        p.single_chunk = cps == 1;
     } else {
         p.nchunk_ub = seq_len / C + batch;
         p.ntile_ub = (p.nchunk_ub + G - 1) / G + batch;
@@ -74,7 +82,7 @@ void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int bloc
     p.off_zero = off;
     off += 512;
     p.off_sink = off;
-    off += 512;
+    off += 1024;
     p.off_chunk_off = off;
     off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));
     p.off_tile_off = off;

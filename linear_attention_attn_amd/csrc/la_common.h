@@ -240,6 +240,10 @@ __device__ __forceinline__ void wg_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Keeps the compiler from hoisting memory accesses across this point (used to
+// bound how many operand fragments are live at once).
+__device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
+
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
 __device__ __forceinline__ uint32_t wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

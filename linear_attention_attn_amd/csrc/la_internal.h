@@ -17,12 +17,13 @@ struct FwdPlan {
     int64_t nchunk_ub = 0;    // chunk slots per head (exact for dense input)
     int64_t ntile_ub = 0;     // scan-tile slots per head
     bool scan_tiles = false;  // some sequence may span more than G chunks
+    bool single_chunk = false;  // every sequence is one chunk: no summaries, no scan
     size_t off_chunk_off = 0; // int32 [nseq + 1]
     size_t off_tile_off = 0;  // int32 [nseq + 1]
     size_t off_states = 0;    // fp32 [heads][nchunk_ub][d][d]
     size_t off_tilesum = 0;   // fp32 [heads][ntile_ub][d][d]
     size_t off_zero = 0;      // 512 bytes, zeroed by the first kernel of every call
-    size_t off_sink = 0;      // 512 bytes that absorb stores of rows past a sequence end
+    size_t off_sink = 0;      // 1024 bytes that absorb stores of rows past a sequence end
     size_t bytes = 0;         // total workspace bytes
 };
 

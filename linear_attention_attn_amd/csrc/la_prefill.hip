@@ -78,7 +78,7 @@ __device__ __forceinline__ int find_seg(const int32_t *off, int n, int64_t x) {
 // chunk_off[s] = sum_{s' < s} ceil(L_s' / C);  tile_off[s] = sum ceil(nc_s' / G).
 constexpr int kPrepThreads = 1024;
 constexpr int kZeroBytes = 512;
-constexpr int kSinkBytes = 512;
+constexpr int kSinkBytes = 1024;   // 64 lanes x 16 bytes
 
 __global__ __launch_bounds__(kPrepThreads) void k_prep(KParams p) {
     __shared__ int64_t sc[kPrepThreads], st[kPrepThreads];
@@ -119,10 +119,10 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(KParams p) {
 
 // ---------------------------------------------------------- tile config
 
-template <typename T, int D, int BLK>
+template <typename T, int D, int BLK, int NWAVES = 8>
 struct Cfg {
     static constexpr int ES = Elem<T>::kBytes;
-    static constexpr int NW = 8, NT = NW * kWave;
+    static constexpr int NW = NWAVES, NT = NW * kWave;
     static constexpr int TJ = ES == 2 ? 64 : 32;        // K/V tokens per LDS tile
     static constexpr int EPC = 16 / ES;                 // elements per 16-byte chunk
     static constexpr int KR_ROW = D * ES;               // row-major K row bytes
@@ -135,25 +135,38 @@ struct Cfg {
     static constexpr int DT = D / 16;                   // 16-wide tiles along d
     static constexpr int KC = D / 32;                   // 32-wide k steps along d
     // state tiles per wave: SA x SB of the DT x DT grid
-    static constexpr int SA = D == 128 ? 2 : 1;
-    static constexpr int SB = D == 128 ? 4 : 2;
+    static constexpr int SA = NW == 16 ? (D == 128 ? 2 : 1) : (D == 128 ? 2 : 1);
+    static constexpr int SB = NW == 16 ? (D == 128 ? 2 : 1) : (D == 128 ? 4 : 2);
     static constexpr int AW = DT / SA;                  // waves along a
     // row slabs (16 rows) of a block handled per wave, and the column split
-    static constexpr int NSW = BLK == 64 ? 1 : 2;
-    static constexpr int CSPLIT = BLK == 256 ? 1 : 2;
+    static constexpr int NSLAB = BLK / 16;
+    static constexpr int NSW = NW == 16 ? 1 : (BLK == 64 ? 1 : 2);
+    static constexpr int CSPLIT = NW * NSW / NSLAB;     // waves sharing one slab (by columns)
     static constexpr int NCT = DT / CSPLIT;             // 16-wide output column tiles per wave
     static_assert(NP <= 256, "patch mapping");
     static_assert(AW * (DT / SB) == NW, "state split");
     static_assert(BLK % TJ == 0, "tile");
+    static_assert(CSPLIT >= 1 && DT % CSPLIT == 0, "column split");
 };
 
-// Row slab (0..BLK/16-1) handled as slab `s` by wave w: pairs of slabs from
-// both ends of the block so that every wave does the same causal work.
-template <int BLK>
+// Row slab (0..BLK/16-1) handled as slab `s` by wave w.  Eight waves: pairs of
+// slabs from both ends of the block so that every wave does the same causal
+// work.  Sixteen waves: one slab each; the four waves of a SIMD (w, w+4, ...)
+// then hold one slab from each quarter of the block.
+template <int BLK, int NW = 8>
 __device__ __forceinline__ int slab_of(int w, int s) {
-    if constexpr (BLK == 256) return s == 0 ? w : 15 - w;
+    if constexpr (NW == 16) return w % (BLK / 16);
+    else if constexpr (BLK == 256) return s == 0 ? w : 15 - w;
     else if constexpr (BLK == 128) return s == 0 ? (w & 3) : 7 - (w & 3);
     else return w & 3;
+}
+
+// First 16-wide output column tile of wave w.
+template <int BLK, int NW, int NCT>
+__device__ __forceinline__ int col_tile0(int w) {
+    constexpr int NSLAB = BLK / 16;
+    if constexpr (NW == 16) return (w / NSLAB) * NCT;
+    else return BLK == 256 ? 0 : (w >> 2) * NCT;
 }
 
 // ------------------------------------------------------ tile staging
@@ -259,6 +272,8 @@ __global__ __launch_bounds__(512, 2) void k_summary(KParams p) {
     const int64_t gch = blockIdx.x;
     if (gch >= p.chunk_off[p.nseq]) return;
     const int s = find_seg(p.chunk_off, p.nseq, gch);
+    // The exclusive prefix never uses the last chunk of a sequence.
+    if (gch + 1 == p.chunk_off[s + 1]) return;
     const Unit u = unit_of<D>(p, s, h);
     const int64_t t0 = (gch - p.chunk_off[s]) * p.chunk;
     const int64_t t1 = min(u.len, t0 + p.chunk);
@@ -542,72 +557,108 @@ __global__ __launch_bounds__(512, 1) void k_fused(KParams p) {
 
 // ================================================================ bf16 path
 // K and V tiles are copied global -> LDS by the DMA engine (no VGPR staging)
-// into a ring of stages, token-major with a 16-byte-chunk swizzle.  Operands
-// that reduce over d (Q K^T) read rows with ds_read_b128; operands that reduce
-// over tokens (P V, K^T V) read columns with ds_read_b64_tr_b16.  Rows past a
-// sequence end are loaded from a zero area, so they add nothing.
+// into a ring of stages.  Operands that reduce over d (Q K^T, Q S) are read
+// as rows with ds_read_b128; operands that reduce over tokens (P V, K^T V)
+// are read as columns with ds_read_b64_tr_b16.  Rows past a sequence end are
+// loaded from a zero area, so they add nothing.
+//
+// LDS layout of a bf16 matrix with ROWS rows (tokens, or state rows):
+// 32-element (64-byte) column blocks, each stored row by row, with the four
+// 16-byte chunks of a 64-byte sub-row rotated by XOR with (row >> 2) & 3:
+//     byte(row, e) = (e / 32) * ROWS * 64 + row * 64
+//                    + (((e % 32) / 8) ^ ((row >> 2) & 3)) * 16 + (e % 8) * 2 .
+// Every operand read below is then a lane-constant base plus a compile-time
+// offset (no per-access address arithmetic), and 16 consecutive rows read at
+// one column hit 16 distinct bank groups.
+template <int ROWS>
+struct SubRows {
+    static constexpr int BLOCK = ROWS * 64;
+    __device__ __forceinline__ static uint32_t off(uint32_t row, uint32_t e) {
+        return (e >> 5) * BLOCK + row * 64 + ((((e & 31) >> 3) ^ ((row >> 2) & 3)) << 4) + (e & 7) * 2;
+    }
+    // Lane base for 8-element row reads (ds_read_b128): row c, elements 8g..8g+7
+    // of column block 0; add block * BLOCK + row0 * 64 (row0 a multiple of 16).
+    __device__ __forceinline__ static uint32_t row8_base(int c, int g) {
+        return c * 64 + ((g ^ ((c >> 2) & 3)) << 4);
+    }
+    // Lane base for column reads (lds_cols8): lane 16g + 4r + q addresses row
+    // 4g + r, elements 16 * par + 4q .. +3 of column block 0 (par = parity of
+    // the 16-column tile); add block * BLOCK + row0 * 64 (row0 a multiple of 32).
+    __device__ __forceinline__ static uint32_t col_base(int l, int par) {
+        const int g = l >> 4, r = (l >> 2) & 3, q = l & 3;
+        return (4 * g + r) * 64 + (((2 * par + (q >> 1)) ^ g) << 4) + (q & 1) * 8;
+    }
+};
 
-template <int D, int TJ>
+template <int D, int TJ, int NW = 8>
 struct DmaTile {
-    static constexpr int RB = D * 2;                 // bytes per token row
-    static constexpr int TB = TJ * RB;               // bytes per tensor tile
+    using L = SubRows<TJ>;
+    static constexpr int TB = TJ * D * 2;            // bytes per tensor tile
     static constexpr int SB = 2 * TB;                // K then V
     static constexpr int NI = TB / 1024;             // 1 KiB wave instructions per tensor
-    static constexpr int IPW = 2 * NI / 8;           // per wave (8 waves)
-    static_assert(TB % 1024 == 0 && (2 * NI) % 8 == 0, "tile split");
+    static constexpr int IPW = 2 * NI / NW;          // per wave
+    static_assert(TB % 1024 == 0 && (2 * NI) % NW == 0 && TJ % 16 == 0, "tile split");
 
-    // Queue the K and V rows [tok0, tok0 + TJ) of a unit into `stage`.
+    // Queue the K and V rows [tok0, tok0 + TJ) of a unit into `stage`.  One
+    // instruction fills 16 rows of one column block: lane l writes row
+    // l / 4, physical chunk l % 4.
     __device__ __forceinline__ static void issue(char *stage, const bf16_t *kb, const bf16_t *vb,
                                                  int64_t tok0, int64_t tend, const bf16_t *zero) {
-        using R = LdsRows<RB>;
         const int w = wave_id(), l = lane_id();
 #pragma unroll
         for (int ii = 0; ii < IPW; ++ii) {
             const int gi = w * IPW + ii;
             const bool isv = gi >= NI;
             const int x = isv ? gi - NI : gi;
-            const uint32_t byte = (uint32_t)x * 1024u + (uint32_t)l * 16u;
-            const uint32_t row = byte / RB;
-            const uint32_t lch = ((byte % RB) >> 4) ^ R::swz(row);
+            const int blk = x / (TJ / 16), row0 = 16 * (x % (TJ / 16));
+            const int row = row0 + (l >> 2);
+            const int lch = (l & 3) ^ ((row >> 2) & 3);
             const int64_t tok = tok0 + row;
-            const bf16_t *src = tok < tend ? (isv ? vb : kb) + tok * D + lch * 8 : zero + lch * 8;
-            dma16(src, stage + (isv ? TB : 0) + x * 1024);
+            const bf16_t *src = tok < tend ? (isv ? vb : kb) + tok * D + blk * 32 + lch * 8 : zero + lch * 8;
+            dma16(src, stage + (isv ? TB : 0) + blk * L::BLOCK + row0 * 64);
         }
     }
 };
 
-// Eight token-strided values of column `col` for MFMA k-slots: slots 0..3 are
-// tokens jb + 4g + (0..3), slots 4..7 tokens jb + 16 + 4g + (0..3) (g = lane/16);
-// the lane's column is col0 + lane % 16.
-template <int RB>
-__device__ __forceinline__ Frag<bf16_t> lds_cols8(const char *tile, int jb, int col0) {
-    using R = LdsRows<RB>;
-    const int l = lane_id(), g = l >> 4, r = (l >> 2) & 3, q = l & 3;
-    const uint32_t b = (uint32_t)(col0 + 4 * q) * 2u;
-    const u32x2_t a0 = lds_read_tr16(tile + R::off(jb + 4 * g + r, b));
-    const u32x2_t a1 = lds_read_tr16(tile + R::off(jb + 16 + 4 * g + r, b));
+template <typename P>
+__device__ __forceinline__ Frag<bf16_t> ld_row8(const char *p) {
+    Frag<bf16_t> f;
+    f.u = *reinterpret_cast<const u32x4_t *>(p);
+    return f;
+}
+// Column read: slots 0..3 from rows +0..3 of the lane's group, slots 4..7
+// from the rows 16 further down (the k-slot order the score tile uses).
+__device__ __forceinline__ Frag<bf16_t> ld_cols8(const char *p) {
+    const u32x2_t a0 = lds_read_tr16(p);
+    const u32x2_t a1 = lds_read_tr16(p + 16 * 64);
     Frag<bf16_t> f;
     f.u = u32x4_t{a0[0], a0[1], a1[0], a1[1]};
     return f;
 }
 
-// S[ia][ib] += K^T V over one token-major tile of TJ tokens.
-template <int D, int TJ, int SA, int SB>
-__device__ __forceinline__ void state_update_tr(f32x4_t (&S)[SA][SB], const char *kt, const char *vt,
-                                                int a0, int b0) {
-    constexpr int RB = D * 2;
+// S[ia][ib] += K^T V over one tile of TJ tokens.  ka[ia] / vb[ib] are the
+// column-read bases of the wave's state rows a and columns b in this stage.
+template <int TJ, int SA, int SB>
+__device__ __forceinline__ void state_update_tr(f32x4_t (&S)[SA][SB], const char *const (&ka)[SA],
+                                                const char *const (&vb)[SB]) {
 #pragma unroll
     for (int jg = 0; jg < TJ / 32; ++jg) {
         Frag<bf16_t> A[SA], B[SB];
 #pragma unroll
-        for (int ia = 0; ia < SA; ++ia) A[ia] = lds_cols8<RB>(kt, jg * 32, (a0 + ia) * 16);
+        for (int ia = 0; ia < SA; ++ia) A[ia] = ld_cols8(ka[ia] + jg * 32 * 64);
 #pragma unroll
-        for (int ib = 0; ib < SB; ++ib) B[ib] = lds_cols8<RB>(vt, jg * 32, (b0 + ib) * 16);
+        for (int ib = 0; ib < SB; ++ib) B[ib] = ld_cols8(vb[ib] + jg * 32 * 64);
 #pragma unroll
         for (int ia = 0; ia < SA; ++ia)
 #pragma unroll
             for (int ib = 0; ib < SB; ++ib) mma(S[ia][ib], A[ia], B[ib]);
     }
+}
+
+// Column-read base, inside a tile, of the 16-column tile `ct` (cols 16ct..).
+template <int ROWS>
+__device__ __forceinline__ uint32_t col_tile_off(int l, int ct) {
+    return SubRows<ROWS>::col_base(l, ct & 1) + (ct >> 1) * SubRows<ROWS>::BLOCK;
 }
 
 // U_c = K_c^T V_c with a two-stage DMA ring (two workgroups fit per CU).
@@ -620,15 +671,22 @@ __global__ __launch_bounds__(512, 2) void k_summary_dma(KParams p) {
     const int64_t gch = blockIdx.x;
     if (gch >= p.chunk_off[p.nseq]) return;
     const int s = find_seg(p.chunk_off, p.nseq, gch);
+    // The exclusive prefix never uses the last chunk of a sequence.
+    if (gch + 1 == p.chunk_off[s + 1]) return;
     const Unit u = unit_of<D>(p, s, h);
     const int64_t t0 = (gch - p.chunk_off[s]) * p.chunk;
     const int64_t t1 = min(u.len, t0 + p.chunk);
-    const bf16_t *kb = reinterpret_cast<const bf16_t *>(p.k) + u.base;
-    const bf16_t *vb = reinterpret_cast<const bf16_t *>(p.v) + u.base;
+    const bf16_t *kbp = reinterpret_cast<const bf16_t *>(p.k) + u.base;
+    const bf16_t *vbp = reinterpret_cast<const bf16_t *>(p.v) + u.base;
     const bf16_t *zero = reinterpret_cast<const bf16_t *>(p.zero);
 
     const int w = wave_id(), l = lane_id(), c = l & 15, g = l >> 4;
     const int a0 = C::SA * (w % C::AW), b0 = C::SB * (w / C::AW);
+    uint32_t ka_off[C::SA], vb_off[C::SB];
+#pragma unroll
+    for (int ia = 0; ia < C::SA; ++ia) ka_off[ia] = col_tile_off<C::TJ>(l, a0 + ia);
+#pragma unroll
+    for (int ib = 0; ib < C::SB; ++ib) vb_off[ib] = DT::TB + col_tile_off<C::TJ>(l, b0 + ib);
     f32x4_t S[C::SA][C::SB];
 #pragma unroll
     for (int ia = 0; ia < C::SA; ++ia)
@@ -636,17 +694,23 @@ __global__ __launch_bounds__(512, 2) void k_summary_dma(KParams p) {
         for (int ib = 0; ib < C::SB; ++ib) S[ia][ib] = zero4();
 
     const int64_t ntile = (t1 - t0 + C::TJ - 1) / C::TJ;
-    DT::issue(lds, kb, vb, t0, t1, zero);
+    DT::issue(lds, kbp, vbp, t0, t1, zero);
     for (int64_t it = 0; it < ntile; ++it) {
-        char *cur = lds + (it & 1) * DT::SB;
+        const char *cur = lds + (it & 1) * DT::SB;
         if (it + 1 < ntile) {
-            DT::issue(lds + ((it + 1) & 1) * DT::SB, kb, vb, t0 + (it + 1) * C::TJ, t1, zero);
+            DT::issue(lds + ((it + 1) & 1) * DT::SB, kbp, vbp, t0 + (it + 1) * C::TJ, t1, zero);
             wait_vm_lgkm0<DT::IPW>();
         } else {
             wait_vm_lgkm0<0>();
         }
         wg_barrier();
-        state_update_tr<D, C::TJ, C::SA, C::SB>(S, cur, cur + DT::TB, a0, b0);
+        const char *ka[C::SA];
+        const char *vb[C::SB];
+#pragma unroll
+        for (int ia = 0; ia < C::SA; ++ia) ka[ia] = cur + ka_off[ia];
+#pragma unroll
+        for (int ib = 0; ib < C::SB; ++ib) vb[ib] = cur + vb_off[ib];
+        state_update_tr<C::TJ, C::SA, C::SB>(S, ka, vb);
         wait_vm_lgkm0<DT::IPW>();   // own LDS reads done (the DMA in flight may stay)
         wg_barrier();               // nobody reads `cur` any more: it may be refilled
     }
@@ -665,15 +729,18 @@ __global__ __launch_bounds__(512, 2) void k_summary_dma(KParams p) {
 // DMA ring (prefetch distance 2).  Every vector-memory instruction a wave
 // issues is unconditional, so the wait before each barrier can name exactly
 // how many younger operations may still be in flight.
-template <int D, int BLK>
-__global__ __launch_bounds__(512, 1) void k_fused_dma(KParams p) {
+template <int D, int BLK, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     using T = bf16_t;
-    using C = Cfg<T, D, BLK>;
-    using DT = DmaTile<D, C::TJ>;
+    using C = Cfg<T, D, BLK, NW>;
+    using DT = DmaTile<D, C::TJ, NW>;
+    using LT = SubRows<C::TJ>;                       // K / V tiles
+    using LS = SubRows<D>;                           // state copy S^T (rows = value dim)
     constexpr int NST = 3;
     constexpr int TPB = BLK / C::TJ;                 // tiles per block
     constexpr int QL = C::NSW * C::KC;               // Q loads per wave per block
-    constexpr int OS = C::NSW * C::NCT;              // O stores per wave per block
+    constexpr int OS = C::NSW * C::NCT / 2;          // O stores per wave per block
+    static_assert(C::NCT % 2 == 0, "column tiles are stored in pairs");
     __shared__ __attribute__((aligned(16))) char lds[NST * DT::SB + C::ST_BYTES];
     char *const st = lds + NST * DT::SB;
 
@@ -694,9 +761,28 @@ __global__ __launch_bounds__(512, 1) void k_fused_dma(KParams p) {
 
     const int w = wave_id(), l = lane_id(), c = l & 15, g = l >> 4;
     const int a0 = C::SA * (w % C::AW), b0 = C::SB * (w / C::AW);
-    const int ct0 = C::CSPLIT == 1 ? 0 : (w >> 2) * C::NCT;
+    const int ct0 = col_tile0<BLK, NW, C::NCT>(w);
     const int64_t ntile = (t1 - t0 + C::TJ - 1) / C::TJ;
     const int64_t nblk = (t1 - t0 + BLK - 1) / BLK;
+
+    // lane-constant LDS offsets
+    const uint32_t row8 = LT::row8_base(c, g);               // == LS::row8_base(c, g)
+    uint32_t ka_off[C::SA], vb_off[C::SB];
+#pragma unroll
+    for (int ia = 0; ia < C::SA; ++ia) ka_off[ia] = col_tile_off<C::TJ>(l, a0 + ia);
+#pragma unroll
+    for (int ib = 0; ib < C::SB; ++ib) vb_off[ib] = DT::TB + col_tile_off<C::TJ>(l, b0 + ib);
+    const uint32_t vpv_off = DT::TB + col_tile_off<C::TJ>(l, ct0);   // ct0 is even
+
+    // state copy S^T: lane writes row b = 16(b0+ib) + c, elements 16(a0+ia) + 4g .. +3
+    auto write_state = [&](const f32x4_t (&Sx)[C::SA][C::SB]) {
+#pragma unroll
+        for (int ia = 0; ia < C::SA; ++ia)
+#pragma unroll
+            for (int ib = 0; ib < C::SB; ++ib)
+                *reinterpret_cast<u32x2_t *>(st + LS::off((b0 + ib) * 16 + c, (a0 + ia) * 16 + 4 * g)) =
+                    u32x2_t{pack_bf16x2(Sx[ia][ib][0], Sx[ia][ib][1]), pack_bf16x2(Sx[ia][ib][2], Sx[ia][ib][3])};
+    };
 
     // ---- state at the chunk start (exclusive prefix from the scan)
     f32x4_t S[C::SA][C::SB];
@@ -710,11 +796,7 @@ __global__ __launch_bounds__(512, 1) void k_fused_dma(KParams p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     S[ia][ib][r] = first ? 0.f : src[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c];
-#pragma unroll
-        for (int ia = 0; ia < C::SA; ++ia)
-#pragma unroll
-            for (int ib = 0; ib < C::SB; ++ib)
-                lds_write4<T, C::ST_ROW>(st, (b0 + ib) * 16 + c, (a0 + ia) * 16 + 4 * g, S[ia][ib]);
+        write_state(S);
     }
 
     // Q fragments of this wave's row slabs (rows past the end re-read the last
@@ -724,7 +806,7 @@ __global__ __launch_bounds__(512, 1) void k_fused_dma(KParams p) {
     auto load_q = [&](int64_t tb) {
 #pragma unroll
         for (int si = 0; si < C::NSW; ++si) {
-            const int64_t row = min(tb + 16 * slab_of<BLK>(w, si) + c, t1 - 1);
+            const int64_t row = min(tb + 16 * slab_of<BLK, NW>(w, si) + c, t1 - 1);
 #pragma unroll
             for (int kc = 0; kc < C::KC; ++kc)
                 Q[si][kc].u = *reinterpret_cast<const u32x4_t *>(qb + row * D + kc * 32 + 8 * g);
@@ -746,23 +828,27 @@ __global__ __launch_bounds__(512, 1) void k_fused_dma(KParams p) {
         const bool more = bi + 1 < nblk;
         const bool dma = t + 2 < ntile;
         if (dma) DT::issue(lds + ((t + 2) % NST) * DT::SB, kb, vb, t0 + (t + 2) * C::TJ, t1, zero);
-        const char *kr = lds + (t % NST) * DT::SB;
-        const char *vr = kr + DT::TB;
+        const char *stage = lds + (t % NST) * DT::SB;
+        const char *krow = stage + row8;          // K rows (b128 reads)
+        const char *vcol = stage + vpv_off;       // V columns of tile ct0 (tr reads)
 
         if (first) {
             // ---- inter-block right product with the block-start state
+            const char *srow = st + row8 + ct0 * 16 * 64;
 #pragma unroll
             for (int si = 0; si < C::NSW; ++si)
 #pragma unroll
                 for (int ct = 0; ct < C::NCT; ++ct) O[si][ct] = zero4();
 #pragma unroll
-            for (int ct = 0; ct < C::NCT; ++ct)
+            for (int ct = 0; ct < C::NCT; ++ct) {
 #pragma unroll
                 for (int kc = 0; kc < C::KC; ++kc) {
-                    const Frag<T> A = lds_read8<T, C::ST_ROW>(st, (ct0 + ct) * 16 + c, kc * 32 + 8 * g);
+                    const Frag<T> A = ld_row8<T>(srow + kc * LS::BLOCK + ct * 16 * 64);
 #pragma unroll
                     for (int si = 0; si < C::NSW; ++si) mma(O[si][ct], A, Q[si][kc]);
                 }
+                if (NW == 16 && (ct & 1)) sched_fence();
+            }
         }
 
         // ---- intra-block left product for this K/V tile
@@ -773,7 +859,7 @@ __global__ __launch_bounds__(512, 1) void k_fused_dma(KParams p) {
             bool need[C::NSW], need1[C::NSW];
 #pragma unroll
             for (int si = 0; si < C::NSW; ++si) {
-                const int i0 = 16 * slab_of<BLK>(w, si);
+                const int i0 = 16 * slab_of<BLK, NW>(w, si);
                 need[si] = jb <= i0 + 15;
                 need1[si] = jb + 16 <= i0 + 15;
                 P[si][0] = zero4();
@@ -787,7 +873,7 @@ __global__ __launch_bounds__(512, 1) void k_fused_dma(KParams p) {
                 if (!any) continue;
 #pragma unroll
                 for (int kc = 0; kc < C::KC; ++kc) {
-                    const Frag<T> A = lds_read8<T, DT::RB>(kr, jg * 32 + 16 * hh + c, kc * 32 + 8 * g);
+                    const Frag<T> A = ld_row8<T>(krow + kc * LT::BLOCK + (jg * 32 + 16 * hh) * 64);
 #pragma unroll
                     for (int si = 0; si < C::NSW; ++si)
                         if (hh ? need1[si] : need[si]) mma(P[si][hh], A, Q[si][kc]);
@@ -796,7 +882,7 @@ __global__ __launch_bounds__(512, 1) void k_fused_dma(KParams p) {
             Frag<T> PF[C::NSW];
 #pragma unroll
             for (int si = 0; si < C::NSW; ++si) {
-                const int i0 = 16 * slab_of<BLK>(w, si);
+                const int i0 = 16 * slab_of<BLK, NW>(w, si);
                 const int i = i0 + c;
                 if (need[si] && jb + 31 > i0) {
 #pragma unroll
@@ -813,40 +899,61 @@ __global__ __launch_bounds__(512, 1) void k_fused_dma(KParams p) {
             if (anyg) {
 #pragma unroll
                 for (int ct = 0; ct < C::NCT; ++ct) {
-                    const Frag<T> A = lds_cols8<DT::RB>(vr, jg * 32, (ct0 + ct) * 16);
+                    // column tile ct0 + ct: parity ct & 1 (ct0 even), block (ct0 + ct) / 2
+                    const char *pcol = vcol + (ct >> 1) * LT::BLOCK + jg * 32 * 64 +
+                                       (ct & 1 ? (int)(col_tile_off<C::TJ>(l, 1) - col_tile_off<C::TJ>(l, 0)) : 0);
+                    const Frag<T> A = ld_cols8(pcol);
 #pragma unroll
                     for (int si = 0; si < C::NSW; ++si)
                         if (need[si]) mma(O[si][ct], A, PF[si]);
+                    if (NW == 16 && (ct & 1)) sched_fence();
                 }
             }
         }
-        // ---- store O: lane holds row (16*slab + c), columns 16*ct + 4g .. +3
+
+        const char *ka[C::SA];
+        const char *vbs[C::SB];
+#pragma unroll
+        for (int ia = 0; ia < C::SA; ++ia) ka[ia] = stage + ka_off[ia];
+#pragma unroll
+        for (int ib = 0; ib < C::SB; ++ib) vbs[ib] = stage + vb_off[ib];
+
+        // ---- store O.  Lane (c, g) holds row 16*slab + c, columns 16*ct + 4g .. +3
+        // of every column tile ct.  Lanes 16 apart (g, g^1) swap one 8-byte half
+        // so that each stores 16 contiguous bytes: the even-g lane the 8 columns
+        // 16*ct + 4g .. +7 of the even tile of a pair, the odd-g lane those of
+        // the odd tile.  Four lanes then cover 64 contiguous bytes of a row.
         auto store_o = [&]() {
+            const bool odd = g & 1;
 #pragma unroll
             for (int si = 0; si < C::NSW; ++si) {
-                const int64_t row = tb + 16 * slab_of<BLK>(w, si) + c;
+                const int64_t row = tb + 16 * slab_of<BLK, NW>(w, si) + c;
                 const bool ok = row < t1;
 #pragma unroll
-                for (int ct = 0; ct < C::NCT; ++ct)
-                    store4(ok ? ob + row * D + (ct0 + ct) * 16 + 4 * g : sink + 4 * l, O[si][ct]);
+                for (int m = 0; m < C::NCT / 2; ++m) {
+                    const uint32_t e0 = pack_bf16x2(O[si][2 * m][0], O[si][2 * m][1]);
+                    const uint32_t e1 = pack_bf16x2(O[si][2 * m][2], O[si][2 * m][3]);
+                    const uint32_t o0 = pack_bf16x2(O[si][2 * m + 1][0], O[si][2 * m + 1][1]);
+                    const uint32_t o1 = pack_bf16x2(O[si][2 * m + 1][2], O[si][2 * m + 1][3]);
+                    const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? e0 : o0), 16);
+                    const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? e1 : o1), 16);
+                    const u32x4_t val = odd ? u32x4_t{r0, r1, o0, o1} : u32x4_t{e0, e1, r0, r1};
+                    const int col = odd ? 16 * (ct0 + 2 * m + 1) + 4 * (g - 1) : 16 * (ct0 + 2 * m) + 4 * g;
+                    *reinterpret_cast<u32x4_t *>(ok ? ob + row * D + col : sink + 8 * l) = val;
+                }
             }
         };
-        auto write_state = [&]() {
-            if (first) {                     // one-tile blocks: the state copy was read this iteration
-                wait_vm_lgkm0<63>();
-                wg_barrier();
-            }
-#pragma unroll
-            for (int ia = 0; ia < C::SA; ++ia)
-#pragma unroll
-                for (int ib = 0; ib < C::SB; ++ib)
-                    lds_write4<T, C::ST_ROW>(st, (b0 + ib) * 16 + c, (a0 + ia) * 16 + 4 * g, S[ia][ib]);
-        };
-        if (last && more) load_q(tb + BLK);
-        if (more) state_update_tr<D, C::TJ, C::SA, C::SB>(S, kr, vr, a0, b0);
+        if (last && more) load_q(tb + BLK);   // Q of this block is dead after the last scores
+        if (more) state_update_tr<C::TJ, C::SA, C::SB>(S, ka, vbs);
         if (last) {
             store_o();
-            if (more) write_state();
+            if (more) {
+                if (first) {                 // one-tile blocks: the state copy was read this iteration
+                    wait_vm_lgkm0<63>();
+                    wg_barrier();
+                }
+                write_state(S);
+            }
         }
         if (t + 1 < ntile) {
             // Tile t+1's DMA was issued before: at the top of iteration t-1 (or in
@@ -868,6 +975,9 @@ __global__ __launch_bounds__(512, 1) void k_fused_dma(KParams p) {
 
 // -------------------------------------------------------------- host side
 
+// Waves per workgroup of the bf16 fused kernel.
+constexpr int fused_waves(int D, int BLK) { return (D == 128 && BLK == 256) ? 16 : 8; }
+
 template <typename T, int D, int BLK>
 static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream_t st, void *const *ev) {
     auto mark = [&](int i) {
@@ -877,21 +987,30 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
     mark(0);
     hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, st, kp);
     mark(1);
-    if constexpr (sizeof(T) == 2)
-        hipLaunchKernelGGL((k_summary_dma<D, BLK>), gchunks, dim3(512), 0, st, kp);
-    else
-        hipLaunchKernelGGL((k_summary<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
-    mark(2);
-    const dim3 gtiles((unsigned)plan.ntile_ub, (D * D) / kScanThreads, (unsigned)kp.heads);
-    if (plan.scan_tiles) {
-        hipLaunchKernelGGL(k_scan_reduce<D>, gtiles, dim3(kScanThreads), 0, st, kp);
-        hipLaunchKernelGGL(k_scan_tiles<D>, dim3(kp.nseq, (D * D) / kScanThreads, kp.heads),
-                           dim3(kScanThreads), 0, st, kp);
+    // Every chunk but the first of its sequence needs the exclusive prefix of
+    // the chunk summaries before it; with one chunk per sequence there is none.
+    if (!plan.single_chunk) {
+        if constexpr (sizeof(T) == 2)
+            hipLaunchKernelGGL((k_summary_dma<D, BLK>), gchunks, dim3(512), 0, st, kp);
+        else
+            hipLaunchKernelGGL((k_summary<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
     }
-    hipLaunchKernelGGL(k_scan_apply<D>, gtiles, dim3(kScanThreads), 0, st, kp, plan.scan_tiles ? 1 : 0);
+    mark(2);
+    if (!plan.single_chunk) {
+        const dim3 gtiles((unsigned)plan.ntile_ub, (D * D) / kScanThreads, (unsigned)kp.heads);
+        if (plan.scan_tiles) {
+            hipLaunchKernelGGL(k_scan_reduce<D>, gtiles, dim3(kScanThreads), 0, st, kp);
+            hipLaunchKernelGGL(k_scan_tiles<D>, dim3(kp.nseq, (D * D) / kScanThreads, kp.heads),
+                               dim3(kScanThreads), 0, st, kp);
+        }
+        hipLaunchKernelGGL(k_scan_apply<D>, gtiles, dim3(kScanThreads), 0, st, kp, plan.scan_tiles ? 1 : 0);
+    }
     mark(3);
     if constexpr (sizeof(T) == 2)
-        hipLaunchKernelGGL((k_fused_dma<D, BLK>), gchunks, dim3(512), 0, st, kp);
+        {
+        constexpr int NWF = fused_waves(D, BLK);
+        hipLaunchKernelGGL((k_fused_dma<D, BLK, NWF>), gchunks, dim3(NWF * 64), 0, st, kp);
+    }
     else
         hipLaunchKernelGGL((k_fused<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
     mark(4);
