@@ -65,6 +65,28 @@ class HipEvents:
             self.lib.hipEventDestroy(e)
 
 
+def profiled_traffic(workload_name):
+    """HBM bytes per launch of the fused kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when that summary is for another
+    workload or the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"k_fused_dma_{workload_name}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.strip().split(":")[0] in ("traffic_bytes_per_launch", "source_sha256"):
+            k, v = line.strip().split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in ("la_prefill.hip", "la_common.h"):
+        with open(os.path.join(ROOT, "linear_attention_attn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def prefill_flops_per_head_token(d, B):
     """Algorithmic work: 2d^2 (Q S) + 2d^2 (K^T V) + 2d(B+1) (causal half of the
     intra-block Q K^T and P V, diagonal included)."""
@@ -287,7 +309,7 @@ def main():
         "workspace_bytes": wsb,
         "roofline": {"bound": "hbm", "kernel": "k_fused (intra-block Q K^T, P V and Q S)",
                      "achieved": fused_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": fused_gbs / PEAK_HBM_GBS, "traffic": None},
+                     "frac": fused_gbs / PEAK_HBM_GBS, "traffic": profiled_traffic(w.name)},
     }
     log(json.dumps({k: out[k] for k in ("value", "ms_per_step", "tflops", "kernels_ms")}))
 
