@@ -245,6 +245,14 @@ __device__ __forceinline__ void wg_barrier() {
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
+// The lane id produced afresh at each call (opaque to the optimiser): values
+// derived from it are recomputed where they are used instead of being held in
+// registers across a loop.
+__device__ __forceinline__ uint32_t lane_id_fresh() {
+    uint32_t l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
 __device__ __forceinline__ uint32_t wave_id() {
     return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
