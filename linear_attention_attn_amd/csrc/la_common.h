@@ -202,6 +202,24 @@ __device__ __forceinline__ void dma16(const void *g, const char *lds) {
                  : "memory", "m0");
 }
 
+// Raw buffer resource over `bytes` bytes at `base` (stride 0): loads past the
+// end return zeros and stores past the end are dropped, by the hardware's
+// range check (offset = voffset + soffset + instruction offset).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Buffer load of 16 bytes per lane straight into LDS: lane l's bytes land at
+// LDS byte m0 + 16 l (lanes out of range write zeros).  Issued from inline asm
+// for the same reason as dma16.
+__device__ __forceinline__ void dma_buf16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                          uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(r), "s"(soff)
+                 : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
 // expcnt 6:4 left at its maximum, lgkmcnt 11:8).
 template <int N>

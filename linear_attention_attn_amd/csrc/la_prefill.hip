@@ -732,68 +732,138 @@ __global__ __launch_bounds__(512, 2) void k_summary_dma(KParams p) {
 }
 
 // Per chunk: walk the blocks carrying S; per block O^T = S^T Q^T + V^T P^T
-// with P = mask(Q K^T), then S += K^T V.  K/V tiles stream through a 3-stage
-// DMA ring (prefetch distance 2).  Every vector-memory instruction a wave
-// issues is unconditional, so the wait before each barrier can name exactly
-// how many younger operations may still be in flight.
+// with P = mask(Q K^T), then S += K^T V.
+//
+// K and V stream through a 4-stage LDS ring in 64-token tiles, loaded by
+// buffer loads straight into LDS; tile t + 3 is requested while tile t is
+// used.  The four tiles of a ring cycle (a "super-block" of 256 tokens, one
+// or more whole blocks) are separate compile-time copies of the tile body, so
+// a tile's stage, its place in its block and its wait counts are constants.
+// All global accesses go through buffer resources that end at the chunk end:
+// rows past it load as zeros (they add nothing to any product) and stores to
+// them are dropped, so a final partial block or super-block is processed as a
+// whole one.
+//
+// Vector-memory order and waits (vmcnt counts in issue order):
+//   tile not ending a block:  DMA(t+3) at its top; at its end wait until at
+//       most 2 tiles of DMA are in flight (DMA(t+1) has landed);
+//   tile ending a block: next block's Q loads after its last scores, O stores
+//       after its P V; at its end wait until only the O stores are in flight
+//       (Q and every older DMA have landed), then DMA(t+3).
+// The compiler sees the Q loads and O stores but not the DMA; since the wait
+// after the Q loads leaves only the compiler-visible O stores in flight, its
+// own bookkeeping never makes a later tile wait for Q (or for the DMA).
 template <int D, int BLK, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     using T = bf16_t;
     using C = Cfg<T, D, BLK, NW>;
-    using DT = DmaTile<D, C::TJ, NW>;
-    using LT = SubRows<C::TJ>;                       // K / V tiles
+    constexpr int TJ = C::TJ;
+    using LT = SubRows<TJ>;                          // K / V tiles
     using LS = SubRows<D>;                           // state copy S^T (rows = value dim)
-    constexpr int NST = 3;
-    constexpr int TPB = BLK / C::TJ;                 // tiles per block
-    constexpr int QL = C::NSW * C::KC;               // Q loads per wave per block
+    constexpr int NST = 4;                           // ring stages = tiles per super-block
+    constexpr int TPB = BLK / TJ;                    // tiles per block
+    constexpr int RB = D * 2;                        // bytes per token row
+    constexpr int TB = TJ * RB;                      // bytes of one tensor tile
+    constexpr int SBY = 2 * TB;                      // stage: K tile then V tile
+    constexpr int NI = TB / 1024;                    // 1 KiB DMA instructions per tensor tile
+    constexpr int IPW = 2 * NI / NW;                 // DMA instructions per wave per tile
     constexpr int OS = C::NSW * C::NCT / 2;          // O stores per wave per block
+    static_assert(NST % TPB == 0 && (2 * NI) % NW == 0 && TB % 1024 == 0, "tile split");
     static_assert(C::NCT % 2 == 0, "column tiles are stored in pairs");
-    __shared__ __attribute__((aligned(16))) char lds[NST * DT::SB + C::ST_BYTES];
-    char *const st = lds + NST * DT::SB;
+    __shared__ __attribute__((aligned(16))) char lds[NST * SBY + C::ST_BYTES];
+    char *const st = lds + NST * SBY;
 
     const int h = blockIdx.y;
-    const int64_t gch = blockIdx.x;
+    const int gch = blockIdx.x;
     if (gch >= p.chunk_off[p.nseq]) return;
     const int s = find_seg(p.chunk_off, p.nseq, gch);
     const Unit u = unit_of<D>(p, s, h);
-    const int64_t cl = gch - p.chunk_off[s];
-    const int64_t t0 = cl * p.chunk;
-    const int64_t t1 = min(u.len, t0 + p.chunk);
-    const T *qb = reinterpret_cast<const T *>(p.q) + u.base;
-    const T *kb = reinterpret_cast<const T *>(p.k) + u.base;
-    const T *vb = reinterpret_cast<const T *>(p.v) + u.base;
-    T *ob = reinterpret_cast<T *>(p.o) + u.base;
-    const T *zero = reinterpret_cast<const T *>(p.zero);
-    T *sink = reinterpret_cast<T *>(p.sink);
+    const int cl = gch - p.chunk_off[s];
+    const int64_t t0 = (int64_t)cl * p.chunk;
+    const int n = (int)min(u.len - t0, p.chunk);     // tokens of this chunk
+    const int64_t cb = (u.base + t0 * D) * 2;        // byte offset of its first row
+    const uint32_t nbytes = (uint32_t)n * RB;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const char *>(p.q) + cb, nbytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const char *>(p.k) + cb, nbytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const char *>(p.v) + cb, nbytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<char *>(p.o) + cb, nbytes);
 
     const int w = wave_id(), l = lane_id(), c = l & 15, g = l >> 4;
     const int a0 = C::SA * (w % C::AW), b0 = C::SB * (w / C::AW);
     const int ct0 = col_tile0<BLK, NW, C::NCT>(w);
-    const int64_t ntile = (t1 - t0 + C::TJ - 1) / C::TJ;
-    const int64_t nblk = (t1 - t0 + BLK - 1) / BLK;
+    const int nblk = (n + BLK - 1) / BLK;
+    const int nsb = (nblk * TPB + NST - 1) / NST;    // super-blocks
 
-    // lane-constant LDS offsets
-    const uint32_t row8 = LT::row8_base(c, g);               // == LS::row8_base(c, g)
+    // ---- lane-constant LDS offsets
+    const uint32_t row8 = LT::row8_base(c, g);       // == LS::row8_base(c, g)
     uint32_t ka_off[C::SA], vb_off[C::SB];
 #pragma unroll
-    for (int ia = 0; ia < C::SA; ++ia) ka_off[ia] = col_tile_off<C::TJ>(l, a0 + ia);
+    for (int ia = 0; ia < C::SA; ++ia) ka_off[ia] = col_tile_off<TJ>(l, a0 + ia);
 #pragma unroll
-    for (int ib = 0; ib < C::SB; ++ib) vb_off[ib] = DT::TB + col_tile_off<C::TJ>(l, b0 + ib);
-    const uint32_t vpv_off = DT::TB + col_tile_off<C::TJ>(l, ct0);   // ct0 is even
+    for (int ib = 0; ib < C::SB; ++ib) vb_off[ib] = TB + col_tile_off<TJ>(l, b0 + ib);
+    const uint32_t vpv_off = TB + col_tile_off<TJ>(l, ct0);       // ct0 is even
+    const int par_step = (int)col_tile_off<TJ>(l, 1) - (int)col_tile_off<TJ>(l, 0);
+
+    // ---- DMA: wave instruction gi = w * IPW + ii fills 16 rows (row0..) of
+    // one 32-element column block of the K (gi < NI) or V tile; lane l brings
+    // row row0 + l / 4, physical 16-byte chunk l % 4.
+    uint32_t dvo[IPW], dm0[IPW];
+    __amdgpu_buffer_rsrc_t drs[IPW];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)lds;
+#pragma unroll
+    for (int ii = 0; ii < IPW; ++ii) {
+        const int gi = w * IPW + ii;
+        const bool isv = gi >= NI;
+        const int x = isv ? gi - NI : gi;
+        const int blk = x / (TJ / 16), row0 = 16 * (x % (TJ / 16));
+        const int row = row0 + (l >> 2);
+        dvo[ii] = (uint32_t)(row * RB + blk * 64 + (((l & 3) ^ LT::swz(row)) << 4));
+        dm0[ii] = lds0 + (isv ? TB : 0) + blk * LT::BLOCK + row0 * 64;
+        drs[ii] = isv ? rv : rk;
+    }
+    auto issue = [&](int tile, int stage) {
+#pragma unroll
+        for (int ii = 0; ii < IPW; ++ii)
+            dma_buf16(drs[ii], dvo[ii], (uint32_t)tile * TB, dm0[ii] + stage * SBY);
+    };
+
+    // ---- Q rows of the wave's slabs: lane (c, g) loads row 16 slab + c,
+    // elements 8g..8g+7 of each 32-element group kc
+    uint32_t qvo[C::NSW], ovo[C::NSW];
+    const bool odd = g & 1;
+#pragma unroll
+    for (int si = 0; si < C::NSW; ++si) {
+        const int r = 16 * slab_of<BLK, NW>(w, si) + c;
+        qvo[si] = (uint32_t)(r * RB + g * 16);
+        // O store m writes columns 16 (ct0 + 2m) + 4g .. +7 (even g) or
+        // 16 (ct0 + 2m + 1) + 4 (g - 1) .. +7 (odd g): 64 m bytes further on
+        ovo[si] = (uint32_t)(r * RB + 2 * (odd ? 16 * (ct0 + 1) + 4 * (g - 1) : 16 * ct0 + 4 * g));
+    }
+    Frag<T> Q[C::NSW][C::KC];
+    auto load_q = [&](int row0) {
+#pragma unroll
+        for (int si = 0; si < C::NSW; ++si)
+#pragma unroll
+            for (int kc = 0; kc < C::KC; ++kc)
+                Q[si][kc].u = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qvo[si] + kc * 64, row0 * RB, 0);
+    };
 
     // state copy S^T: lane writes row b = 16(b0+ib) + c, elements 16(a0+ia) + 4g .. +3
     auto write_state = [&](const f32x4_t (&Sx)[C::SA][C::SB]) {
-        const int l = lane_id_fresh(), c = l & 15, g = l >> 4;
+        const int lf = lane_id_fresh(), cf = lf & 15, gf = lf >> 4;
 #pragma unroll
         for (int ia = 0; ia < C::SA; ++ia)
 #pragma unroll
             for (int ib = 0; ib < C::SB; ++ib)
-                *reinterpret_cast<u32x2_t *>(st + LS::off((b0 + ib) * 16 + c, (a0 + ia) * 16 + 4 * g)) =
+                *reinterpret_cast<u32x2_t *>(st + LS::off((b0 + ib) * 16 + cf, (a0 + ia) * 16 + 4 * gf)) =
                     u32x2_t{pack_bf16x2(Sx[ia][ib][0], Sx[ia][ib][1]), pack_bf16x2(Sx[ia][ib][2], Sx[ia][ib][3])};
     };
 
-    // ---- state at the chunk start (exclusive prefix from the scan)
+    // ---- prologue: the first block's Q, tile 0, the state at the chunk start
+    // (exclusive prefix from the scan; zero for a sequence's first chunk)
     f32x4_t S[C::SA][C::SB];
+    load_q(0);
+    issue(0, 0);
     {
         const float *src = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
         const bool first = cl == 0;
@@ -806,49 +876,34 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
                     S[ia][ib][r] = first ? 0.f : src[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c];
         write_state(S);
     }
-
-    // Q fragments of this wave's row slabs (rows past the end re-read the last
-    // row: their outputs are never stored and each query row only feeds its
-    // own output row)
-    Frag<T> Q[C::NSW][C::KC];
-    auto load_q = [&](int64_t tb) {
-#pragma unroll
-        for (int si = 0; si < C::NSW; ++si) {
-            const int64_t row = min(tb + 16 * slab_of<BLK, NW>(w, si) + c, t1 - 1);
-#pragma unroll
-            for (int kc = 0; kc < C::KC; ++kc)
-                Q[si][kc].u = *reinterpret_cast<const u32x4_t *>(qb + row * D + kc * 32 + 8 * g);
-        }
-    };
-    load_q(t0);
-    DT::issue(lds, kb, vb, t0, t1, zero);
-    wait_vm_lgkm0<0>();              // Q, the start state and tile 0 are in
-    if (ntile > 1) DT::issue(lds + DT::SB, kb, vb, t0 + C::TJ, t1, zero);
+    wait_vm_lgkm0<0>();
+    issue(1, 1);
+    issue(2, 2);
     wg_barrier();
 
     f32x4_t O[C::NSW][C::NCT];
-    for (int64_t t = 0; t < ntile; ++t) {
-        const int jt = (int)(t % TPB);
-        const int64_t bi = t / TPB;
-        const int64_t tb = t0 + bi * BLK;
-        const bool first = jt == 0;
-        const bool last = jt == TPB - 1 || t == ntile - 1;
-        const bool more = bi + 1 < nblk;
-        const bool dma = t + 2 < ntile;
-        if (dma) DT::issue(lds + ((t + 2) % NST) * DT::SB, kb, vb, t0 + (t + 2) * C::TJ, t1, zero);
-        const char *stage = lds + (t % NST) * DT::SB;
-        const char *krow = stage + row8;          // K rows (b128 reads)
-        const char *vcol = stage + vpv_off;       // V columns of tile ct0 (tr reads)
+    using std::integral_constant;
 
-        if (first) {
+    auto tile = [&](auto J_c, int sb) {
+        constexpr int J = decltype(J_c)::value;     // tile within the super-block = ring stage
+        constexpr int jt = J % TPB;                  // tile within its block
+        constexpr bool first = jt == 0, last = jt == TPB - 1;
+        const int t = sb * NST + J;
+        const int bi = sb * (NST / TPB) + J / TPB;
+        const int tb = bi * BLK;                     // block's first token (chunk-relative)
+        const bool more = bi + 1 < nblk;
+        if constexpr (!last) issue(t + 3, (J + 3) % NST);
+        const char *stage = lds + J * SBY;
+        const char *krow = stage + row8;             // K rows (b128 reads)
+        const char *vcol = stage + vpv_off;          // V columns of tile ct0 (tr reads)
+
+        if constexpr (first) {
             // ---- inter-block right product with the block-start state
             const char *srow = st + row8 + ct0 * 16 * 64;
 #pragma unroll
-            for (int si = 0; si < C::NSW; ++si)
-#pragma unroll
-                for (int ct = 0; ct < C::NCT; ++ct) O[si][ct] = zero4();
-#pragma unroll
             for (int ct = 0; ct < C::NCT; ++ct) {
+#pragma unroll
+                for (int si = 0; si < C::NSW; ++si) O[si][ct] = zero4();
 #pragma unroll
                 for (int kc = 0; kc < C::KC; ++kc) {
                     const Frag<T> A = ld_row8<T>(srow + kc * LS::BLOCK + ct * 16 * 64);
@@ -861,8 +916,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
 
         // ---- intra-block left product for this K/V tile
 #pragma unroll
-        for (int jg = 0; jg < C::TJ / 32; ++jg) {
-            const int jb = jt * C::TJ + jg * 32;          // block-local first token of the group
+        for (int jg = 0; jg < TJ / 32; ++jg) {
+            constexpr int jt_ = jt;
+            const int jb = jt_ * TJ + jg * 32;       // block-local first token of the group
             f32x4_t P[C::NSW][2];
             bool need[C::NSW], need1[C::NSW];
 #pragma unroll
@@ -886,6 +942,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
                     for (int si = 0; si < C::NSW; ++si)
                         if (hh ? need1[si] : need[si]) mma(P[si][hh], A, Q[si][kc]);
                 }
+                if (NW == 16) sched_fence();
             }
             Frag<T> PF[C::NSW];
 #pragma unroll
@@ -908,8 +965,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
 #pragma unroll
                 for (int ct = 0; ct < C::NCT; ++ct) {
                     // column tile ct0 + ct: parity ct & 1 (ct0 even), block (ct0 + ct) / 2
-                    const char *pcol = vcol + (ct >> 1) * LT::BLOCK + jg * 32 * 64 +
-                                       (ct & 1 ? (int)(col_tile_off<C::TJ>(l, 1) - col_tile_off<C::TJ>(l, 0)) : 0);
+                    const char *pcol = vcol + (ct >> 1) * LT::BLOCK + jg * 32 * 64 + (ct & 1 ? par_step : 0);
                     const Frag<T> A = ld_cols8(pcol);
 #pragma unroll
                     for (int si = 0; si < C::NSW; ++si)
@@ -926,18 +982,22 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
 #pragma unroll
         for (int ib = 0; ib < C::SB; ++ib) vbs[ib] = stage + vb_off[ib];
 
-        // ---- store O.  Lane (c, g) holds row 16*slab + c, columns 16*ct + 4g .. +3
-        // of every column tile ct.  Lanes 16 apart (g, g^1) swap one 8-byte half
-        // so that each stores 16 contiguous bytes: the even-g lane the 8 columns
-        // 16*ct + 4g .. +7 of the even tile of a pair, the odd-g lane those of
-        // the odd tile.  Four lanes then cover 64 contiguous bytes of a row.
-        auto store_o = [&]() {
-            const int l = lane_id_fresh(), c = l & 15, g = l >> 4;
-            const bool odd = g & 1;
+        if constexpr (last) {
+            load_q(tb + BLK);                        // this block's Q is dead after its last scores
+            // ---- store O.  Lane (c, g) holds row 16 slab + c, columns
+            // 16 ct + 4g .. +3 of every column tile ct.  Lanes 16 apart (g, g^1)
+            // swap one 8-byte half so that each stores 16 contiguous bytes: the
+            // even-g lane columns 16 ct + 4g .. +7 of the even tile of a pair,
+            // the odd-g lane those of the odd tile.  Four lanes cover 64
+            // contiguous bytes of a row.
 #pragma unroll
             for (int si = 0; si < C::NSW; ++si) {
-                const int64_t row = tb + 16 * slab_of<BLK, NW>(w, si) + c;
-                const bool ok = row < t1;
+                // The block offset goes into the lane offset, not the scalar
+                // one: with a register scalar offset the compiler does not
+                // separate a 16-byte buffer store from a following write of
+                // its data registers, and the store then picks up the new
+                // values in some lanes.
+                const int vo = (int)ovo[si] + tb * RB;
 #pragma unroll
                 for (int m = 0; m < C::NCT / 2; ++m) {
                     const uint32_t e0 = pack_bf16x2(O[si][2 * m][0], O[si][2 * m][1]);
@@ -947,39 +1007,33 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
                     const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? e0 : o0), 16);
                     const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? e1 : o1), 16);
                     const u32x4_t val = odd ? u32x4_t{r0, r1, o0, o1} : u32x4_t{e0, e1, r0, r1};
-                    const int col = odd ? 16 * (ct0 + 2 * m + 1) + 4 * (g - 1) : 16 * (ct0 + 2 * m) + 4 * g;
-                    *reinterpret_cast<u32x4_t *>(ok ? ob + row * D + col : sink + 8 * l) = val;
+                    __builtin_amdgcn_raw_buffer_store_b128(val, ro, vo + m * 64, 0, 0);
                 }
             }
-        };
-        // Tile t+1's DMA was issued at the top of tile t-1 (or in the
-        // prologue).  At the end of a block only this tile's O stores may stay
-        // in flight, so the next block's Q has landed before the barrier: the
-        // compiler then never waits for Q inside later tiles, where its wait
-        // would also cover the DMA it cannot see.  The Q loads are issued
-        // unconditionally (past the last block the rows clamp to the last
-        // token) so that every path from them meets that wait, and the wait
-        // also follows the last tile.  Elsewhere this tile's DMA may stay in
-        // flight, and the previous tile's O stores if that tile ended a block.
-        if (last) {
-            load_q(tb + BLK);               // Q of this block is dead after the last scores
-            store_o();                       // frees O before the state update needs registers
-            if (more) state_update_tr<C::TJ, C::SA, C::SB>(S, ka, vbs);
             if (more) {
-                if (first) {                 // one-tile blocks: the state copy was read this iteration
+                state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
+                if constexpr (first) {               // one-tile blocks: the state copy was read in this tile
                     wait_vm_lgkm0<63>();
                     wg_barrier();
                 }
                 write_state(S);
             }
-            wait_vm_lgkm0<OS>();
+            wait_vm_lgkm0<OS>();                     // Q and all DMA so far have landed
+            issue(t + 3, (J + 3) % NST);
         } else {
-            if (more) state_update_tr<C::TJ, C::SA, C::SB>(S, ka, vbs);
-            const bool lastp = t > 0 && (int)((t - 1) % TPB) == TPB - 1;
-            wait_vm_lgkm0((dma ? DT::IPW : 0) + (lastp ? OS : 0));
+            if (more) state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
+            wait_vm_lgkm0<2 * IPW>();                // DMA(t + 1) has landed
         }
         wg_barrier();
+    };
+
+    for (int sb = 0; sb < nsb; ++sb) {
+        tile(integral_constant<int, 0>{}, sb);
+        tile(integral_constant<int, 1>{}, sb);
+        tile(integral_constant<int, 2>{}, sb);
+        tile(integral_constant<int, 3>{}, sb);
     }
+    wait_vm_lgkm0<0>();                              // DMA past the chunk end has landed
 }
 
 // -------------------------------------------------------------- host side
