@@ -744,15 +744,21 @@ __global__ __launch_bounds__(512, 2) void k_summary_dma(KParams p) {
 // them are dropped, so a final partial block or super-block is processed as a
 // whole one.
 //
-// Vector-memory order and waits (vmcnt counts in issue order):
-//   tile not ending a block:  DMA(t+3) at its top; at its end wait until at
-//       most 2 tiles of DMA are in flight (DMA(t+1) has landed);
-//   tile ending a block: next block's Q loads after its last scores, O stores
-//       after its P V; at its end wait until only the O stores are in flight
-//       (Q and every older DMA have landed), then DMA(t+3).
-// The compiler sees the Q loads and O stores but not the DMA; since the wait
-// after the Q loads leaves only the compiler-visible O stores in flight, its
-// own bookkeeping never makes a later tile wait for Q (or for the DMA).
+// Vector-memory order and waits.  vmcnt counts loads and stores together;
+// loads complete in issue order, but stores may complete before older loads,
+// so every wait below bounds only the number of loads that may still be in
+// flight younger than the one it needs:
+//   a block's O is stored at the top of the next block's first tile (after
+//   that tile's DMA), so no store is outstanding at a block's last tile;
+//   with two or more tiles per block the next block's Q is loaded one tile
+//   before the block's last (into Qn), else after the last scores;
+//   tile not ending a block: DMA(t+3) at its top; at its end DMA(t+1) must
+//   have landed, behind it may be DMA(t+2), DMA(t+3) and the next Q;
+//   tile ending a block: wait for every load (the next Q and DMA up to t+2),
+//   then request DMA(t+3).
+// The compiler sees the Q loads and O stores but not the DMA; the full wait
+// at the end of each block retires the Q loads in its bookkeeping too, so it
+// never makes a later tile wait for them (or for the DMA it cannot see).
 template <int D, int BLK, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     using T = bf16_t;
@@ -839,13 +845,18 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         // 16 (ct0 + 2m + 1) + 4 (g - 1) .. +7 (odd g): 64 m bytes further on
         ovo[si] = (uint32_t)(r * RB + 2 * (odd ? 16 * (ct0 + 1) + 4 * (g - 1) : 16 * ct0 + 4 * g));
     }
-    Frag<T> Q[C::NSW][C::KC];
-    auto load_q = [&](int row0) {
+    // Q of the current block, and of the next one: with two or more tiles per
+    // block the next block's Q is requested one tile before the block ends,
+    // so its latency hides behind that tile's work.
+    constexpr int QL = C::NSW * C::KC;               // Q loads per wave per block
+    constexpr int JPF = TPB >= 2 ? TPB - 2 : -1;     // tile of a block that requests the next Q
+    Frag<T> Q[C::NSW][C::KC], Qn[C::NSW][C::KC];
+    auto load_q = [&](Frag<T> (&dst)[C::NSW][C::KC], int row0) {
 #pragma unroll
         for (int si = 0; si < C::NSW; ++si)
 #pragma unroll
             for (int kc = 0; kc < C::KC; ++kc)
-                Q[si][kc].u = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qvo[si] + kc * 64, row0 * RB, 0);
+                dst[si][kc].u = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qvo[si] + kc * 64, row0 * RB, 0);
     };
 
     // state copy S^T: lane writes row b = 16(b0+ib) + c, elements 16(a0+ia) + 4g .. +3
@@ -862,7 +873,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     // ---- prologue: the first block's Q, tile 0, the state at the chunk start
     // (exclusive prefix from the scan; zero for a sequence's first chunk)
     f32x4_t S[C::SA][C::SB];
-    load_q(0);
+    load_q(Q, 0);
     issue(0, 0);
     {
         const float *src = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
@@ -876,12 +887,40 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
                     S[ia][ib][r] = first ? 0.f : src[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c];
         write_state(S);
     }
-    wait_vm_lgkm0<0>();
     issue(1, 1);
+    wait_vm_lgkm0<0>();
     issue(2, 2);
     wg_barrier();
 
     f32x4_t O[C::NSW][C::NCT];
+    // ---- store the O of block bi.  Lane (c, g) holds row 16 slab + c, columns
+    // 16 ct + 4g .. +3 of every column tile ct.  Lanes 16 apart (g, g^1) swap
+    // one 8-byte half so that each stores 16 contiguous bytes: the even-g lane
+    // columns 16 ct + 4g .. +7 of the even tile of a pair, the odd-g lane those
+    // of the odd tile.  Four lanes cover 64 contiguous bytes of a row.
+    auto store_o = [&](int bi) {
+#pragma unroll
+        for (int si = 0; si < C::NSW; ++si) {
+            // The block offset goes into the lane offset, not the scalar
+            // one: with a register scalar offset the compiler does not
+            // separate a 16-byte buffer store from a following write of
+            // its data registers, and the store then picks up the new
+            // values in some lanes.
+            const int vo = (int)ovo[si] + bi * BLK * RB;
+#pragma unroll
+            for (int m = 0; m < C::NCT / 2; ++m) {
+                const uint32_t e0 = pack_bf16x2(O[si][2 * m][0], O[si][2 * m][1]);
+                const uint32_t e1 = pack_bf16x2(O[si][2 * m][2], O[si][2 * m][3]);
+                const uint32_t o0 = pack_bf16x2(O[si][2 * m + 1][0], O[si][2 * m + 1][1]);
+                const uint32_t o1 = pack_bf16x2(O[si][2 * m + 1][2], O[si][2 * m + 1][3]);
+                const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? e0 : o0), 16);
+                const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? e1 : o1), 16);
+                const u32x4_t val = odd ? u32x4_t{r0, r1, o0, o1} : u32x4_t{e0, e1, r0, r1};
+                __builtin_amdgcn_raw_buffer_store_b128(val, ro, vo + m * 64, 0, 0);
+            }
+        }
+    };
+
     using std::integral_constant;
 
     auto tile = [&](auto J_c, int sb) {
@@ -892,7 +931,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         const int bi = sb * (NST / TPB) + J / TPB;
         const int tb = bi * BLK;                     // block's first token (chunk-relative)
         const bool more = bi + 1 < nblk;
+        constexpr bool pf = jt == JPF;
         if constexpr (!last) issue(t + 3, (J + 3) % NST);
+        if constexpr (first) {
+            if (bi > 0) store_o(bi - 1);
+        }
+        if constexpr (pf) load_q(Qn, tb + BLK);
         const char *stage = lds + J * SBY;
         const char *krow = stage + row8;             // K rows (b128 reads)
         const char *vcol = stage + vpv_off;          // V columns of tile ct0 (tr reads)
@@ -983,33 +1027,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         for (int ib = 0; ib < C::SB; ++ib) vbs[ib] = stage + vb_off[ib];
 
         if constexpr (last) {
-            load_q(tb + BLK);                        // this block's Q is dead after its last scores
-            // ---- store O.  Lane (c, g) holds row 16 slab + c, columns
-            // 16 ct + 4g .. +3 of every column tile ct.  Lanes 16 apart (g, g^1)
-            // swap one 8-byte half so that each stores 16 contiguous bytes: the
-            // even-g lane columns 16 ct + 4g .. +7 of the even tile of a pair,
-            // the odd-g lane those of the odd tile.  Four lanes cover 64
-            // contiguous bytes of a row.
-#pragma unroll
-            for (int si = 0; si < C::NSW; ++si) {
-                // The block offset goes into the lane offset, not the scalar
-                // one: with a register scalar offset the compiler does not
-                // separate a 16-byte buffer store from a following write of
-                // its data registers, and the store then picks up the new
-                // values in some lanes.
-                const int vo = (int)ovo[si] + tb * RB;
-#pragma unroll
-                for (int m = 0; m < C::NCT / 2; ++m) {
-                    const uint32_t e0 = pack_bf16x2(O[si][2 * m][0], O[si][2 * m][1]);
-                    const uint32_t e1 = pack_bf16x2(O[si][2 * m][2], O[si][2 * m][3]);
-                    const uint32_t o0 = pack_bf16x2(O[si][2 * m + 1][0], O[si][2 * m + 1][1]);
-                    const uint32_t o1 = pack_bf16x2(O[si][2 * m + 1][2], O[si][2 * m + 1][3]);
-                    const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? e0 : o0), 16);
-                    const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? e1 : o1), 16);
-                    const u32x4_t val = odd ? u32x4_t{r0, r1, o0, o1} : u32x4_t{e0, e1, r0, r1};
-                    __builtin_amdgcn_raw_buffer_store_b128(val, ro, vo + m * 64, 0, 0);
-                }
-            }
+            if constexpr (TPB == 1) load_q(Q, tb + BLK);   // this block's Q is dead after its last scores
             if (more) {
                 state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
                 if constexpr (first) {               // one-tile blocks: the state copy was read in this tile
@@ -1018,11 +1036,18 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
                 }
                 write_state(S);
             }
-            wait_vm_lgkm0<OS>();                     // Q and all DMA so far have landed
+            wait_vm_lgkm0<0>();                      // the next Q and all DMA so far have landed
             issue(t + 3, (J + 3) % NST);
+            if constexpr (TPB > 1) {
+#pragma unroll
+                for (int si = 0; si < C::NSW; ++si)
+#pragma unroll
+                    for (int kc = 0; kc < C::KC; ++kc) Q[si][kc] = Qn[si][kc];
+            }
         } else {
             if (more) state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
-            wait_vm_lgkm0<2 * IPW>();                // DMA(t + 1) has landed
+            // DMA(t + 1) has landed (in a block's first tile it already had)
+            wait_vm_lgkm0<2 * IPW + (pf ? QL : 0) + (first ? OS : 0)>();
         }
         wg_barrier();
     };
@@ -1033,6 +1058,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         tile(integral_constant<int, 2>{}, sb);
         tile(integral_constant<int, 3>{}, sb);
     }
+    store_o(nsb * (NST / TPB) - 1);
     wait_vm_lgkm0<0>();                              // DMA past the chunk end has landed
 }
 
