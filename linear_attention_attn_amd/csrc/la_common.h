@@ -258,6 +258,15 @@ __device__ __forceinline__ void wg_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Makes the fragments' registers live (and their loads complete) at this
+// point, so a batch of LDS reads is issued back to back and waited for once
+// instead of being interleaved one by one with the products that use them.
+template <int N, typename F>
+__device__ __forceinline__ void hold(const F (&f)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : : "v"(f[i].u));
+}
+
 // Keeps the compiler from hoisting memory accesses across this point (used to
 // bound how many operand fragments are live at once).
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }

@@ -750,10 +750,9 @@ __global__ __launch_bounds__(512, 2) void k_summary_dma(KParams p) {
 // flight younger than the one it needs:
 //   a block's O is stored at the top of the next block's first tile (after
 //   that tile's DMA), so no store is outstanding at a block's last tile;
-//   with two or more tiles per block the next block's Q is loaded one tile
-//   before the block's last (into Qn), else after the last scores;
+//   the next block's Q is loaded after the block's last scores;
 //   tile not ending a block: DMA(t+3) at its top; at its end DMA(t+1) must
-//   have landed, behind it may be DMA(t+2), DMA(t+3) and the next Q;
+//   have landed, behind it may be DMA(t+2) and DMA(t+3);
 //   tile ending a block: wait for every load (the next Q and DMA up to t+2),
 //   then request DMA(t+3).
 // The compiler sees the Q loads and O stores but not the DMA; the full wait
@@ -845,18 +844,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         // 16 (ct0 + 2m + 1) + 4 (g - 1) .. +7 (odd g): 64 m bytes further on
         ovo[si] = (uint32_t)(r * RB + 2 * (odd ? 16 * (ct0 + 1) + 4 * (g - 1) : 16 * ct0 + 4 * g));
     }
-    // Q of the current block, and of the next one: with two or more tiles per
-    // block the next block's Q is requested one tile before the block ends,
-    // so its latency hides behind that tile's work.
-    constexpr int QL = C::NSW * C::KC;               // Q loads per wave per block
-    constexpr int JPF = TPB >= 2 ? TPB - 2 : -1;     // tile of a block that requests the next Q
-    Frag<T> Q[C::NSW][C::KC], Qn[C::NSW][C::KC];
-    auto load_q = [&](Frag<T> (&dst)[C::NSW][C::KC], int row0) {
+    Frag<T> Q[C::NSW][C::KC];
+    auto load_q = [&](int row0) {
 #pragma unroll
         for (int si = 0; si < C::NSW; ++si)
 #pragma unroll
             for (int kc = 0; kc < C::KC; ++kc)
-                dst[si][kc].u = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qvo[si] + kc * 64, row0 * RB, 0);
+                Q[si][kc].u = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qvo[si] + kc * 64, row0 * RB, 0);
     };
 
     // state copy S^T: lane writes row b = 16(b0+ib) + c, elements 16(a0+ia) + 4g .. +3
@@ -873,7 +867,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     // ---- prologue: the first block's Q, tile 0, the state at the chunk start
     // (exclusive prefix from the scan; zero for a sequence's first chunk)
     f32x4_t S[C::SA][C::SB];
-    load_q(Q, 0);
+    load_q(0);
     issue(0, 0);
     {
         const float *src = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
@@ -931,12 +925,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         const int bi = sb * (NST / TPB) + J / TPB;
         const int tb = bi * BLK;                     // block's first token (chunk-relative)
         const bool more = bi + 1 < nblk;
-        constexpr bool pf = jt == JPF;
         if constexpr (!last) issue(t + 3, (J + 3) % NST);
         if constexpr (first) {
             if (bi > 0) store_o(bi - 1);
         }
-        if constexpr (pf) load_q(Qn, tb + BLK);
         const char *stage = lds + J * SBY;
         const char *krow = stage + row8;             // K rows (b128 reads)
         const char *vcol = stage + vpv_off;          // V columns of tile ct0 (tr reads)
@@ -946,15 +938,19 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
             const char *srow = st + row8 + ct0 * 16 * 64;
 #pragma unroll
             for (int ct = 0; ct < C::NCT; ++ct) {
+                // all KC fragments of the column tile are requested before the
+                // first product, so one LDS latency covers KC products
+                Frag<T> A[C::KC];
+#pragma unroll
+                for (int kc = 0; kc < C::KC; ++kc) A[kc] = ld_row8<T>(srow + kc * LS::BLOCK + ct * 16 * 64);
+                hold(A);
 #pragma unroll
                 for (int si = 0; si < C::NSW; ++si) O[si][ct] = zero4();
 #pragma unroll
-                for (int kc = 0; kc < C::KC; ++kc) {
-                    const Frag<T> A = ld_row8<T>(srow + kc * LS::BLOCK + ct * 16 * 64);
+                for (int kc = 0; kc < C::KC; ++kc)
 #pragma unroll
-                    for (int si = 0; si < C::NSW; ++si) mma(O[si][ct], A, Q[si][kc]);
-                }
-                if (NW == 16 && (ct & 1)) sched_fence();
+                    for (int si = 0; si < C::NSW; ++si) mma(O[si][ct], A[kc], Q[si][kc]);
+                sched_fence();
             }
         }
 
@@ -979,14 +975,16 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
 #pragma unroll
                 for (int si = 0; si < C::NSW; ++si) any |= hh ? need1[si] : need[si];
                 if (!any) continue;
+                Frag<T> A[C::KC];
 #pragma unroll
-                for (int kc = 0; kc < C::KC; ++kc) {
-                    const Frag<T> A = ld_row8<T>(krow + kc * LT::BLOCK + (jg * 32 + 16 * hh) * 64);
+                for (int kc = 0; kc < C::KC; ++kc) A[kc] = ld_row8<T>(krow + kc * LT::BLOCK + (jg * 32 + 16 * hh) * 64);
+                hold(A);
+#pragma unroll
+                for (int kc = 0; kc < C::KC; ++kc)
 #pragma unroll
                     for (int si = 0; si < C::NSW; ++si)
-                        if (hh ? need1[si] : need[si]) mma(P[si][hh], A, Q[si][kc]);
-                }
-                if (NW == 16) sched_fence();
+                        if (hh ? need1[si] : need[si]) mma(P[si][hh], A[kc], Q[si][kc]);
+                sched_fence();
             }
             Frag<T> PF[C::NSW];
 #pragma unroll
@@ -1006,15 +1004,25 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
 #pragma unroll
             for (int si = 0; si < C::NSW; ++si) anyg |= need[si];
             if (anyg) {
+                // batches of PB column tiles: their V fragments are requested
+                // together, then PB products
+                constexpr int PB = C::NCT < 4 ? C::NCT : 4;
 #pragma unroll
-                for (int ct = 0; ct < C::NCT; ++ct) {
-                    // column tile ct0 + ct: parity ct & 1 (ct0 even), block (ct0 + ct) / 2
-                    const char *pcol = vcol + (ct >> 1) * LT::BLOCK + jg * 32 * 64 + (ct & 1 ? par_step : 0);
-                    const Frag<T> A = ld_cols8(pcol);
+                for (int cb = 0; cb < C::NCT; cb += PB) {
+                    Frag<T> A[PB];
 #pragma unroll
-                    for (int si = 0; si < C::NSW; ++si)
-                        if (need[si]) mma(O[si][ct], A, PF[si]);
-                    if (NW == 16 && (ct & 1)) sched_fence();
+                    for (int b = 0; b < PB; ++b) {
+                        // column tile ct0 + ct: parity ct & 1 (ct0 even), block (ct0 + ct) / 2
+                        const int ct = cb + b;
+                        A[b] = ld_cols8(vcol + (ct >> 1) * LT::BLOCK + jg * 32 * 64 + (ct & 1 ? par_step : 0));
+                    }
+                    hold(A);
+#pragma unroll
+                    for (int b = 0; b < PB; ++b)
+#pragma unroll
+                        for (int si = 0; si < C::NSW; ++si)
+                            if (need[si]) mma(O[si][cb + b], A[b], PF[si]);
+                    sched_fence();
                 }
             }
         }
@@ -1027,7 +1035,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         for (int ib = 0; ib < C::SB; ++ib) vbs[ib] = stage + vb_off[ib];
 
         if constexpr (last) {
-            if constexpr (TPB == 1) load_q(Q, tb + BLK);   // this block's Q is dead after its last scores
+            load_q(tb + BLK);                        // this block's Q is dead after its last scores
             if (more) {
                 state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
                 if constexpr (first) {               // one-tile blocks: the state copy was read in this tile
@@ -1038,16 +1046,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
             }
             wait_vm_lgkm0<0>();                      // the next Q and all DMA so far have landed
             issue(t + 3, (J + 3) % NST);
-            if constexpr (TPB > 1) {
-#pragma unroll
-                for (int si = 0; si < C::NSW; ++si)
-#pragma unroll
-                    for (int kc = 0; kc < C::KC; ++kc) Q[si][kc] = Qn[si][kc];
-            }
         } else {
             if (more) state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
             // DMA(t + 1) has landed (in a block's first tile it already had)
-            wait_vm_lgkm0<2 * IPW + (pf ? QL : 0) + (first ? OS : 0)>();
+            wait_vm_lgkm0<2 * IPW + (first ? OS : 0)>();
         }
         wg_barrier();
     };
