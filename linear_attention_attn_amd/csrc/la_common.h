@@ -220,6 +220,33 @@ __device__ __forceinline__ void dma_buf16(__amdgpu_buffer_rsrc_t r, uint32_t vof
                  : "memory", "m0");
 }
 
+// Buffer load of 16 bytes per lane straight into LDS (lane l's bytes at
+// lds + 16 l), visible to the compiler: it tracks the LDS destination and
+// waits for this load before an LDS access that may read it.
+__device__ __forceinline__ void dma_lds16(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}
+
+// 16-byte buffer store from inline asm, so that the compiler's vmcnt
+// bookkeeping holds loads only (it treats a counter with loads and stores
+// pending as unordered and then waits for everything).  The s_nop keeps the
+// data registers unchanged for the wait state a store of more than 8 bytes
+// needs before they are written again.
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u32x4_t v) {
+    asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 1"
+                 :
+                 : "v"(v), "v"(voff), "s"(r)
+                 : "memory");
+}
+
+// 8-byte LDS write from inline asm.  Used for LDS that the compiler would
+// otherwise order behind pending LDS DMA (with a full vmcnt wait) although
+// the DMA writes elsewhere; the caller's lgkmcnt wait and barrier publish it.
+__device__ __forceinline__ void lds_store8(char *p, u32x2_t v) {
+    const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)p;
+    asm volatile("ds_write_b64 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+
 // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
 // expcnt 6:4 left at its maximum, lgkmcnt 11:8).
 template <int N>

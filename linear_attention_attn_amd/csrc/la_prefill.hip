@@ -731,6 +731,20 @@ __global__ __launch_bounds__(512, 2) void k_summary_dma(KParams p) {
                 dst[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c] = S[ia][ib][r];
 }
 
+// Which 32-element groups [lo(jt), hi(jt)) of the next block's Q a wave
+// requests in tile jt of a block with TPB tiles (none in the last tile), and
+// how many loads that is (n(-1) = 0: the tile before a block's first).
+template <int TPB, int KC, int NSW>
+struct QSplit {
+    static constexpr int lo(int jt) {
+        return TPB == 4 ? (jt == 0 ? 0 : jt == 1 ? KC / 4 : jt == 2 ? KC / 2 : KC) : (TPB == 2 && jt == 0 ? 0 : KC);
+    }
+    static constexpr int hi(int jt) {
+        return TPB == 4 ? (jt == 0 ? KC / 4 : jt == 1 ? KC / 2 : KC) : (TPB == 2 && jt == 0 ? KC : KC);
+    }
+    static constexpr int n(int jt) { return jt < 0 ? 0 : NSW * (hi(jt) - lo(jt)); }
+};
+
 // Per chunk: walk the blocks carrying S; per block O^T = S^T Q^T + V^T P^T
 // with P = mask(Q K^T), then S += K^T V.
 //
@@ -744,20 +758,26 @@ __global__ __launch_bounds__(512, 2) void k_summary_dma(KParams p) {
 // them are dropped, so a final partial block or super-block is processed as a
 // whole one.
 //
-// Vector-memory order and waits.  vmcnt counts loads and stores together;
-// loads complete in issue order, but stores may complete before older loads,
-// so every wait below bounds only the number of loads that may still be in
-// flight younger than the one it needs:
-//   a block's O is stored at the top of the next block's first tile (after
-//   that tile's DMA), so no store is outstanding at a block's last tile;
-//   the next block's Q is loaded after the block's last scores;
+// Vector-memory order and waits.  The ring stages are separate LDS arrays,
+// so the compiler tracks each DMA by its destination and itself waits exactly
+// for the loads a read needs (DMA, Q); O stores are issued from inline asm and
+// stay outside its bookkeeping, which would otherwise treat loads and stores
+// as unordered.  vmcnt counts both; loads complete in issue order but stores
+// may complete ahead of older loads, so each explicit wait (the one before a
+// barrier, which other waves rely on) bounds the loads younger than the one
+// it needs:
+//   the next block's Q is loaded over the block's tiles, each part at the
+//   top of a tile ahead of its DMA;
 //   tile not ending a block: DMA(t+3) at its top; at its end DMA(t+1) must
-//   have landed, behind it may be DMA(t+2) and DMA(t+3);
-//   tile ending a block: wait for every load (the next Q and DMA up to t+2),
-//   then request DMA(t+3).
-// The compiler sees the Q loads and O stores but not the DMA; the full wait
-// at the end of each block retires the Q loads in its bookkeeping too, so it
-// never makes a later tile wait for them (or for the DMA it cannot see).
+//   have landed; younger are DMA(t+2), DMA(t+3) and the Q loads of this
+//   tile and the one before;
+//   tile ending a block: all of the next Q and DMA(t+1) must have landed;
+//   younger is the DMA of the tile before; then it requests DMA(t+3);
+//   a wave stores its O after the wait of the last tile that holds keys of
+//   its rows (O is final there), so the stores spread over the block and
+//   complete during the following tile.
+// With one tile per block the next Q is loaded after the tile's scores and
+// the tile waits for every load.
 template <int D, int BLK, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     using T = bf16_t;
@@ -772,11 +792,20 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     constexpr int SBY = 2 * TB;                      // stage: K tile then V tile
     constexpr int NI = TB / 1024;                    // 1 KiB DMA instructions per tensor tile
     constexpr int IPW = 2 * NI / NW;                 // DMA instructions per wave per tile
-    constexpr int OS = C::NSW * C::NCT / 2;          // O stores per wave per block
+    constexpr int QL = C::NSW * C::KC;               // Q loads per wave per block
+    // The next block's Q is requested over the tiles of a block, a few
+    // fragments per tile ahead of that tile's DMA: 32-element groups
+    // [qlo(jt), qhi(jt)) in tile jt (none in the last tile; with one tile per
+    // block Q is instead reloaded after that tile's scores).
+    using QS = QSplit<TPB, C::KC, C::NSW>;
     static_assert(NST % TPB == 0 && (2 * NI) % NW == 0 && TB % 1024 == 0, "tile split");
     static_assert(C::NCT % 2 == 0, "column tiles are stored in pairs");
-    __shared__ __attribute__((aligned(16))) char lds[NST * SBY + C::ST_BYTES];
-    char *const st = lds + NST * SBY;
+    __shared__ __attribute__((aligned(16))) char stage0[SBY];
+    __shared__ __attribute__((aligned(16))) char stage1[SBY];
+    __shared__ __attribute__((aligned(16))) char stage2[SBY];
+    __shared__ __attribute__((aligned(16))) char stage3[SBY];
+    __shared__ __attribute__((aligned(16))) char st[C::ST_BYTES];
+    char *const stages[NST] = {stage0, stage1, stage2, stage3};
 
     const int h = blockIdx.y;
     const int gch = blockIdx.x;
@@ -812,9 +841,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     // ---- DMA: wave instruction gi = w * IPW + ii fills 16 rows (row0..) of
     // one 32-element column block of the K (gi < NI) or V tile; lane l brings
     // row row0 + l / 4, physical 16-byte chunk l % 4.
-    uint32_t dvo[IPW], dm0[IPW];
+    uint32_t dvo[IPW], dlo[IPW];
     __amdgpu_buffer_rsrc_t drs[IPW];
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)lds;
 #pragma unroll
     for (int ii = 0; ii < IPW; ++ii) {
         const int gi = w * IPW + ii;
@@ -823,13 +851,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         const int blk = x / (TJ / 16), row0 = 16 * (x % (TJ / 16));
         const int row = row0 + (l >> 2);
         dvo[ii] = (uint32_t)(row * RB + blk * 64 + (((l & 3) ^ LT::swz(row)) << 4));
-        dm0[ii] = lds0 + (isv ? TB : 0) + blk * LT::BLOCK + row0 * 64;
+        dlo[ii] = (isv ? TB : 0) + blk * LT::BLOCK + row0 * 64;
         drs[ii] = isv ? rv : rk;
     }
-    auto issue = [&](int tile, int stage) {
+    auto issue = [&](int tile, char *stage) {
 #pragma unroll
         for (int ii = 0; ii < IPW; ++ii)
-            dma_buf16(drs[ii], dvo[ii], (uint32_t)tile * TB, dm0[ii] + stage * SBY);
+            dma_lds16(drs[ii], stage + dlo[ii], dvo[ii], (uint32_t)(tile * TB));
     };
 
     // ---- Q rows of the wave's slabs: lane (c, g) loads row 16 slab + c,
@@ -844,14 +872,24 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         // 16 (ct0 + 2m + 1) + 4 (g - 1) .. +7 (odd g): 64 m bytes further on
         ovo[si] = (uint32_t)(r * RB + 2 * (odd ? 16 * (ct0 + 1) + 4 * (g - 1) : 16 * ct0 + 4 * g));
     }
-    Frag<T> Q[C::NSW][C::KC];
-    auto load_q = [&](int row0) {
+    // Q of the current block, and of the next one (requested a tile early
+    // when blocks have two or more tiles)
+    Frag<T> Q[C::NSW][C::KC], Qn[C::NSW][C::KC];
+    auto load_q = [&](Frag<T> (&dst)[C::NSW][C::KC], int row0, int k0, int k1) {
 #pragma unroll
         for (int si = 0; si < C::NSW; ++si)
 #pragma unroll
             for (int kc = 0; kc < C::KC; ++kc)
-                Q[si][kc].u = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qvo[si] + kc * 64, row0 * RB, 0);
+                if (kc >= k0 && kc < k1)
+                    dst[si][kc].u = __builtin_amdgcn_raw_buffer_load_b128(rq, (int)qvo[si] + kc * 64, row0 * RB, 0);
     };
+    // Tile of a block after which the wave's O is final and its Q unused:
+    // the last tile holding keys of its last row slab.  The wave stores its O
+    // there, so the stores of a block spread over its tiles.
+    int smax = 0;
+#pragma unroll
+    for (int si = 0; si < C::NSW; ++si) smax = max(smax, slab_of<BLK, NW>(w, si));
+    const int jl = min(TPB - 1, (16 * smax + 15) / TJ);
 
     // state copy S^T: lane writes row b = 16(b0+ib) + c, elements 16(a0+ia) + 4g .. +3
     auto write_state = [&](const f32x4_t (&Sx)[C::SA][C::SB]) {
@@ -860,15 +898,17 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         for (int ia = 0; ia < C::SA; ++ia)
 #pragma unroll
             for (int ib = 0; ib < C::SB; ++ib)
-                *reinterpret_cast<u32x2_t *>(st + LS::off((b0 + ib) * 16 + cf, (a0 + ia) * 16 + 4 * gf)) =
-                    u32x2_t{pack_bf16x2(Sx[ia][ib][0], Sx[ia][ib][1]), pack_bf16x2(Sx[ia][ib][2], Sx[ia][ib][3])};
+                lds_store8(st + LS::off((b0 + ib) * 16 + cf, (a0 + ia) * 16 + 4 * gf),
+                           u32x2_t{pack_bf16x2(Sx[ia][ib][0], Sx[ia][ib][1]), pack_bf16x2(Sx[ia][ib][2], Sx[ia][ib][3])});
     };
 
-    // ---- prologue: the first block's Q, tile 0, the state at the chunk start
-    // (exclusive prefix from the scan; zero for a sequence's first chunk)
+    // ---- prologue: the first block's Q, tiles 0 and 1, the state at the
+    // chunk start (exclusive prefix from the scan; zero for a sequence's
+    // first chunk); tile 2 stays in flight
     f32x4_t S[C::SA][C::SB];
-    load_q(0);
-    issue(0, 0);
+    load_q(Q, 0, 0, C::KC);
+    issue(0, stages[0]);
+    issue(1, stages[1]);
     {
         const float *src = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
         const bool first = cl == 0;
@@ -881,9 +921,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
                     S[ia][ib][r] = first ? 0.f : src[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c];
         write_state(S);
     }
-    issue(1, 1);
     wait_vm_lgkm0<0>();
-    issue(2, 2);
+    issue(2, stages[2]);
     wg_barrier();
 
     f32x4_t O[C::NSW][C::NCT];
@@ -895,11 +934,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     auto store_o = [&](int bi) {
 #pragma unroll
         for (int si = 0; si < C::NSW; ++si) {
-            // The block offset goes into the lane offset, not the scalar
-            // one: with a register scalar offset the compiler does not
-            // separate a 16-byte buffer store from a following write of
-            // its data registers, and the store then picks up the new
-            // values in some lanes.
             const int vo = (int)ovo[si] + bi * BLK * RB;
 #pragma unroll
             for (int m = 0; m < C::NCT / 2; ++m) {
@@ -910,7 +944,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
                 const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? e0 : o0), 16);
                 const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? e1 : o1), 16);
                 const u32x4_t val = odd ? u32x4_t{r0, r1, o0, o1} : u32x4_t{e0, e1, r0, r1};
-                __builtin_amdgcn_raw_buffer_store_b128(val, ro, vo + m * 64, 0, 0);
+                store16(ro, (uint32_t)(vo + m * 64), val);
             }
         }
     };
@@ -925,11 +959,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         const int bi = sb * (NST / TPB) + J / TPB;
         const int tb = bi * BLK;                     // block's first token (chunk-relative)
         const bool more = bi + 1 < nblk;
-        if constexpr (!last) issue(t + 3, (J + 3) % NST);
-        if constexpr (first) {
-            if (bi > 0) store_o(bi - 1);
-        }
-        const char *stage = lds + J * SBY;
+        if constexpr (QS::n(jt) > 0) load_q(Qn, tb + BLK, QS::lo(jt), QS::hi(jt));
+        if constexpr (!last) issue(t + 3, stages[(J + 3) % NST]);
+        const char *stage = stages[J];
         const char *krow = stage + row8;             // K rows (b128 reads)
         const char *vcol = stage + vpv_off;          // V columns of tile ct0 (tr reads)
 
@@ -1035,7 +1067,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         for (int ib = 0; ib < C::SB; ++ib) vbs[ib] = stage + vb_off[ib];
 
         if constexpr (last) {
-            load_q(tb + BLK);                        // this block's Q is dead after its last scores
+            if constexpr (TPB == 1) load_q(Q, tb + BLK, 0, C::KC);   // this block's Q is dead after its scores
             if (more) {
                 state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
                 if constexpr (first) {               // one-tile blocks: the state copy was read in this tile
@@ -1044,13 +1076,23 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
                 }
                 write_state(S);
             }
-            wait_vm_lgkm0<0>();                      // the next Q and all DMA so far have landed
-            issue(t + 3, (J + 3) % NST);
+            if constexpr (TPB == 1) {
+                wait_vm_lgkm0<0>();
+            } else {
+                wait_vm_lgkm0<IPW>();                // the next Q and DMA(t+1) have landed
+#pragma unroll
+                for (int si = 0; si < C::NSW; ++si)
+#pragma unroll
+                    for (int kc = 0; kc < C::KC; ++kc) Q[si][kc] = Qn[si][kc];
+            }
+            issue(t + 3, stages[(J + 3) % NST]);
         } else {
             if (more) state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
-            // DMA(t + 1) has landed (in a block's first tile it already had)
-            wait_vm_lgkm0<2 * IPW + (first ? OS : 0)>();
+            // DMA(t+1) has landed; younger are two tiles of DMA and the Q
+            // loads of this tile and the one before
+            wait_vm_lgkm0<2 * IPW + QS::n(jt) + QS::n(jt - 1)>();
         }
+        if (jt == jl) store_o(bi);
         wg_barrier();
     };
 
@@ -1060,8 +1102,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         tile(integral_constant<int, 2>{}, sb);
         tile(integral_constant<int, 3>{}, sb);
     }
-    store_o(nsb * (NST / TPB) - 1);
-    wait_vm_lgkm0<0>();                              // DMA past the chunk end has landed
+    wait_vm_lgkm0<0>();                              // DMA past the chunk end and the stores are done
 }
 
 // -------------------------------------------------------------- host side
