@@ -79,10 +79,6 @@ void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int bloc
     }
     const size_t dd = (size_t)head_dim * head_dim * sizeof(float);
     size_t off = 0;
-    p.off_zero = off;
-    off += 512;
-    p.off_sink = off;
-    off += 1024;
     p.off_chunk_off = off;
     off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));
     p.off_tile_off = off;

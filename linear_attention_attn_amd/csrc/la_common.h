@@ -184,40 +184,11 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const char *p) {
     return __builtin_bit_cast(u32x2_t, r);
 }
 
-// 16 bytes from global memory to LDS for every lane of the wave: lane l's
-// bytes land at lds + 16 * l (lds must be wave-uniform).  No VGPR holds the
-// data and the load counts in vmcnt like any vector-memory load.
-//
-// Issued from inline assembly on purpose: the compiler then does not track
-// the LDS write, so it does not make every later LDS read wait for all
-// outstanding DMA (the callers wait for exactly the stage they read with
-// wait_vm_lgkm0 + wg_barrier).  The compiler also does not count these loads
-// in its own vmcnt bookkeeping for register loads; that only makes its waits
-// stricter than needed, never looser, since the hardware count is larger.
-__device__ __forceinline__ void dma16(const void *g, const char *lds) {
-    const uint32_t m0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)lds;
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(g), "s"(m0)
-                 : "memory", "m0");
-}
-
 // Raw buffer resource over `bytes` bytes at `base` (stride 0): loads past the
 // end return zeros and stores past the end are dropped, by the hardware's
 // range check (offset = voffset + soffset + instruction offset).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Buffer load of 16 bytes per lane straight into LDS: lane l's bytes land at
-// LDS byte m0 + 16 l (lanes out of range write zeros).  Issued from inline asm
-// for the same reason as dma16.
-__device__ __forceinline__ void dma_buf16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                          uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"(m0), "v"(voff), "s"(r), "s"(soff)
-                 : "memory", "m0");
 }
 
 // Buffer load of 16 bytes per lane straight into LDS (lane l's bytes at

@@ -22,8 +22,6 @@ struct FwdPlan {
     size_t off_tile_off = 0;  // int32 [nseq + 1]
     size_t off_states = 0;    // fp32 [heads][nchunk_ub][d][d]
     size_t off_tilesum = 0;   // fp32 [heads][ntile_ub][d][d]
-    size_t off_zero = 0;      // 512 bytes, zeroed by the first kernel of every call
-    size_t off_sink = 0;      // 1024 bytes that absorb stores of rows past a sequence end
     size_t bytes = 0;         // total workspace bytes
 };
 

@@ -35,8 +35,6 @@ struct KParams {
     int32_t *tile_off;      // [nseq + 1]
     float *states;          // [heads][nchunk_ub][D*D]
     float *tilesum;         // [heads][ntile_ub][D*D]
-    uint32_t *zero;         // kZeroBytes of zeros (rows past a sequence end are loaded from here)
-    uint32_t *sink;         // kSinkBytes: target of the stores of rows past a sequence end
     int64_t seq_len;        // dense: per sequence; packed: total tokens
     int64_t chunk;          // tokens per chunk
     int64_t nchunk_ub, ntile_ub;
@@ -77,8 +75,6 @@ __device__ __forceinline__ int find_seg(const int32_t *off, int n, int64_t x) {
 // -------------------------------------------------------------- k_prep
 // chunk_off[s] = sum_{s' < s} ceil(L_s' / C);  tile_off[s] = sum ceil(nc_s' / G).
 constexpr int kPrepThreads = 1024;
-constexpr int kZeroBytes = 512;
-constexpr int kSinkBytes = 1024;   // 64 lanes x 16 bytes
 
 __global__ __launch_bounds__(kPrepThreads) void k_prep(KParams p) {
     __shared__ int64_t sc[kPrepThreads], st[kPrepThreads];
@@ -93,7 +89,6 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(KParams p) {
         g += (nc + p.group - 1) / p.group;
     }
     sc[t] = c; st[t] = g;
-    if (t < kZeroBytes / 4) p.zero[t] = 0u;
     __syncthreads();
     for (int d = 1; d < kPrepThreads; d <<= 1) {   // inclusive Hillis-Steele scan
         int64_t a = t >= d ? sc[t - d] : 0, b = t >= d ? st[t - d] : 0;
@@ -556,11 +551,11 @@ __global__ __launch_bounds__(512, 1) void k_fused(KParams p) {
 }
 
 // ================================================================ bf16 path
-// K and V tiles are copied global -> LDS by the DMA engine (no VGPR staging)
-// into a ring of stages.  Operands that reduce over d (Q K^T, Q S) are read
-// as rows with ds_read_b128; operands that reduce over tokens (P V, K^T V)
-// are read as columns with ds_read_b64_tr_b16.  Rows past a sequence end are
-// loaded from a zero area, so they add nothing.
+// K and V tiles are buffer-loaded straight into LDS (no VGPR staging) into a
+// ring of stages.  Operands that reduce over d (Q K^T, Q S) are read as rows
+// with ds_read_b128; operands that reduce over tokens (P V, K^T V) are read as
+// columns with ds_read_b64_tr_b16.  The buffer resources end at the chunk end:
+// rows past it load as zeros, so they add nothing.
 //
 // LDS layout of a bf16 matrix with ROWS rows (tokens, or state rows):
 // 32-element (64-byte) column blocks, each stored row by row, with the four
@@ -594,36 +589,6 @@ struct SubRows {
     __device__ __forceinline__ static uint32_t col_base(int l, int par) {
         const int g = l >> 4, r = (l >> 2) & 3, q = l & 3;
         return (4 * g + r) * 64 + (((2 * par + (q >> 1)) ^ swz(4 * g + r)) << 4) + (q & 1) * 8;
-    }
-};
-
-template <int D, int TJ, int NW = 8>
-struct DmaTile {
-    using L = SubRows<TJ>;
-    static constexpr int TB = TJ * D * 2;            // bytes per tensor tile
-    static constexpr int SB = 2 * TB;                // K then V
-    static constexpr int NI = TB / 1024;             // 1 KiB wave instructions per tensor
-    static constexpr int IPW = 2 * NI / NW;          // per wave
-    static_assert(TB % 1024 == 0 && (2 * NI) % NW == 0 && TJ % 16 == 0, "tile split");
-
-    // Queue the K and V rows [tok0, tok0 + TJ) of a unit into `stage`.  One
-    // instruction fills 16 rows of one column block: lane l writes row
-    // l / 4, physical chunk l % 4.
-    __device__ __forceinline__ static void issue(char *stage, const bf16_t *kb, const bf16_t *vb,
-                                                 int64_t tok0, int64_t tend, const bf16_t *zero) {
-        const int w = wave_id(), l = lane_id_fresh();
-#pragma unroll
-        for (int ii = 0; ii < IPW; ++ii) {
-            const int gi = w * IPW + ii;
-            const bool isv = gi >= NI;
-            const int x = isv ? gi - NI : gi;
-            const int blk = x / (TJ / 16), row0 = 16 * (x % (TJ / 16));
-            const int row = row0 + (l >> 2);
-            const int lch = (l & 3) ^ L::swz(row);
-            const int64_t tok = tok0 + row;
-            const bf16_t *src = tok < tend ? (isv ? vb : kb) + tok * D + blk * 32 + lch * 8 : zero + lch * 8;
-            dma16(src, stage + (isv ? TB : 0) + blk * L::BLOCK + row0 * 64);
-        }
     }
 };
 
@@ -668,48 +633,77 @@ __device__ __forceinline__ uint32_t col_tile_off(int l, int ct) {
     return SubRows<ROWS>::col_base(l, ct & 1) + (ct >> 1) * SubRows<ROWS>::BLOCK;
 }
 
-// U_c = K_c^T V_c with a two-stage DMA ring (two workgroups fit per CU).
+// U_c = K_c^T V_c over a chunk.  K/V tiles of 64 tokens are buffer-loaded
+// straight into a two-stage LDS ring (two workgroups fit per CU); the buffer
+// resources end at the chunk end, so rows past it load as zeros.  The stages
+// are separate LDS arrays so the compiler tracks each DMA by destination.
 template <int D, int BLK>
 __global__ __launch_bounds__(512, 2) void k_summary_dma(KParams p) {
     using C = Cfg<bf16_t, D, BLK>;
-    using DT = DmaTile<D, C::TJ>;
-    __shared__ __attribute__((aligned(16))) char lds[2 * DT::SB];
+    constexpr int TJ = C::TJ;
+    using LT = SubRows<TJ>;
+    constexpr int NW = 8;
+    constexpr int RB = D * 2;                        // bytes per token row
+    constexpr int TB = TJ * RB;                      // bytes of one tensor tile
+    constexpr int SBY = 2 * TB;                      // stage: K tile then V tile
+    constexpr int NI = TB / 1024;                    // 1 KiB DMA instructions per tensor tile
+    constexpr int IPW = 2 * NI / NW;                 // per wave per tile
+    static_assert((2 * NI) % NW == 0 && TB % 1024 == 0, "tile split");
+    __shared__ __attribute__((aligned(16))) char stage0[SBY];
+    __shared__ __attribute__((aligned(16))) char stage1[SBY];
+    char *const stages[2] = {stage0, stage1};
     const int h = blockIdx.y;
-    const int64_t gch = blockIdx.x;
+    const int gch = blockIdx.x;
     if (gch >= p.chunk_off[p.nseq]) return;
     const int s = find_seg(p.chunk_off, p.nseq, gch);
     // The exclusive prefix never uses the last chunk of a sequence.
     if (gch + 1 == p.chunk_off[s + 1]) return;
     const Unit u = unit_of<D>(p, s, h);
-    const int64_t t0 = (gch - p.chunk_off[s]) * p.chunk;
-    const int64_t t1 = min(u.len, t0 + p.chunk);
-    const bf16_t *kbp = reinterpret_cast<const bf16_t *>(p.k) + u.base;
-    const bf16_t *vbp = reinterpret_cast<const bf16_t *>(p.v) + u.base;
-    const bf16_t *zero = reinterpret_cast<const bf16_t *>(p.zero);
+    const int64_t t0 = (int64_t)(gch - p.chunk_off[s]) * p.chunk;
+    const int n = (int)min(u.len - t0, p.chunk);     // tokens of this chunk
+    const int64_t cb = (u.base + t0 * D) * 2;
+    const uint32_t nbytes = (uint32_t)n * RB;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const char *>(p.k) + cb, nbytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const char *>(p.v) + cb, nbytes);
 
     const int w = wave_id(), l = lane_id(), c = l & 15, g = l >> 4;
     const int a0 = C::SA * (w % C::AW), b0 = C::SB * (w / C::AW);
     uint32_t ka_off[C::SA], vb_off[C::SB];
 #pragma unroll
-    for (int ia = 0; ia < C::SA; ++ia) ka_off[ia] = col_tile_off<C::TJ>(l, a0 + ia);
+    for (int ia = 0; ia < C::SA; ++ia) ka_off[ia] = col_tile_off<TJ>(l, a0 + ia);
 #pragma unroll
-    for (int ib = 0; ib < C::SB; ++ib) vb_off[ib] = DT::TB + col_tile_off<C::TJ>(l, b0 + ib);
+    for (int ib = 0; ib < C::SB; ++ib) vb_off[ib] = TB + col_tile_off<TJ>(l, b0 + ib);
+
+    // DMA: wave instruction gi = w * IPW + ii fills 16 rows of one 32-element
+    // column block of the K (gi < NI) or V tile (as in the fused kernel)
+    uint32_t dvo[IPW], dlo[IPW];
+    __amdgpu_buffer_rsrc_t drs[IPW];
+#pragma unroll
+    for (int ii = 0; ii < IPW; ++ii) {
+        const int gi = w * IPW + ii;
+        const bool isv = gi >= NI;
+        const int x = isv ? gi - NI : gi;
+        const int blk = x / (TJ / 16), row0 = 16 * (x % (TJ / 16));
+        const int row = row0 + (l >> 2);
+        dvo[ii] = (uint32_t)(row * RB + blk * 64 + (((l & 3) ^ LT::swz(row)) << 4));
+        dlo[ii] = (isv ? TB : 0) + blk * LT::BLOCK + row0 * 64;
+        drs[ii] = isv ? rv : rk;
+    }
+    auto issue = [&](int tile, char *stage) {
+#pragma unroll
+        for (int ii = 0; ii < IPW; ++ii) dma_lds16(drs[ii], stage + dlo[ii], dvo[ii], (uint32_t)(tile * TB));
+    };
+
     f32x4_t S[C::SA][C::SB];
 #pragma unroll
     for (int ia = 0; ia < C::SA; ++ia)
 #pragma unroll
         for (int ib = 0; ib < C::SB; ++ib) S[ia][ib] = zero4();
 
-    const int64_t ntile = (t1 - t0 + C::TJ - 1) / C::TJ;
-    DT::issue(lds, kbp, vbp, t0, t1, zero);
-    for (int64_t it = 0; it < ntile; ++it) {
-        const char *cur = lds + (it & 1) * DT::SB;
-        if (it + 1 < ntile) {
-            DT::issue(lds + ((it + 1) & 1) * DT::SB, kbp, vbp, t0 + (it + 1) * C::TJ, t1, zero);
-            wait_vm_lgkm0<DT::IPW>();
-        } else {
-            wait_vm_lgkm0<0>();
-        }
+    const int ntile = (n + TJ - 1) / TJ;
+    auto step = [&](int it, char *cur, char *nxt) {
+        issue(it + 1, nxt);                          // past the end: zeros, never read
+        wait_vm_lgkm0<IPW>();                        // tile it has landed
         wg_barrier();
         const char *ka[C::SA];
         const char *vb[C::SB];
@@ -717,10 +711,16 @@ __global__ __launch_bounds__(512, 2) void k_summary_dma(KParams p) {
         for (int ia = 0; ia < C::SA; ++ia) ka[ia] = cur + ka_off[ia];
 #pragma unroll
         for (int ib = 0; ib < C::SB; ++ib) vb[ib] = cur + vb_off[ib];
-        state_update_tr<C::TJ, C::SA, C::SB>(S, ka, vb);
-        wait_vm_lgkm0<DT::IPW>();   // own LDS reads done (the DMA in flight may stay)
-        wg_barrier();               // nobody reads `cur` any more: it may be refilled
+        state_update_tr<TJ, C::SA, C::SB>(S, ka, vb);
+        wait_vm_lgkm0<IPW>();                        // own LDS reads done (the next DMA may stay)
+        wg_barrier();                                // nobody reads `cur` any more: it may be refilled
+    };
+    issue(0, stages[0]);
+    for (int it = 0; it < ntile; it += 2) {
+        step(it, stages[0], stages[1]);
+        if (it + 1 < ntile) step(it + 1, stages[1], stages[0]);
     }
+    wait_vm_lgkm0<0>();                              // the DMA past the end has landed
     float *dst = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
 #pragma unroll
     for (int ia = 0; ia < C::SA; ++ia)
@@ -1167,8 +1167,6 @@ int launch_fwd(const FwdArgs &a, void *stream, void *const *events) {
     kp.tile_off = reinterpret_cast<int32_t *>(a.workspace + a.plan.off_tile_off);
     kp.states = reinterpret_cast<float *>(a.workspace + a.plan.off_states);
     kp.tilesum = reinterpret_cast<float *>(a.workspace + a.plan.off_tilesum);
-    kp.zero = reinterpret_cast<uint32_t *>(a.workspace + a.plan.off_zero);
-    kp.sink = reinterpret_cast<uint32_t *>(a.workspace + a.plan.off_sink);
     kp.seq_len = a.seq_len;
     kp.chunk = a.plan.chunk;
     kp.nchunk_ub = a.plan.nchunk_ub;
