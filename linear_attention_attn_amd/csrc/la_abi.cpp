@@ -53,14 +53,20 @@ void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int bloc
     const int64_t lavg = std::max<int64_t>(1, varlen ? seq_len / batch : seq_len);
     const int64_t per_cu = std::max<int64_t>(1, units * lavg / kCUs);
     int64_t C;
-    if (!varlen && per_cu >= seq_len) {
+    // One chunk per sequence while the chunk's rows stay within the 32-bit
+    // buffer offsets of the bf16 kernels (2^30 bytes, with margin).
+    const bool fits = seq_len * (int64_t)head_dim * 2 <= ((int64_t)1 << 30);
+    if (!varlen && per_cu >= seq_len && fits) {
         C = (seq_len + block_size - 1) / block_size * block_size;   // one chunk per sequence
     } else {
         C = block_size;
         while (C * 2 <= kMaxChunk && C * 2 <= per_cu) C *= 2;
     }
     const int64_t forced = env_i64("LA_CHUNK_TOKENS", 0);
-    if (forced > 0) C = std::max<int64_t>(block_size, forced / block_size * block_size);
+    if (forced > 0) {
+        const int64_t cap = (((int64_t)1 << 30) / (head_dim * 2)) / block_size * block_size;
+        C = std::max<int64_t>(block_size, std::min(cap, forced / block_size * block_size));
+    }
 
     const int G = 32;
     FwdPlan p;
