@@ -8,6 +8,9 @@
 // 4 d^2 flops), so it is bound by HBM bandwidth: one workgroup per state,
 // every thread streams 16-byte column groups of whole 512-byte rows, and the
 // read-modify-write of S and the q.S partial sums come from the same load.
+// The state is touched once per step and is far larger than the caches, so
+// its loads and stores are non-temporal (streaming); measured on MI355X this
+// is about 10% faster than cached accesses at 256 x 64 heads.
 #include <hip/hip_runtime.h>
 
 #include "la_common.h"
@@ -51,7 +54,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const T *__restrict__ q,
     f32x4_t s[RPT];
 #pragma unroll
     for (int m = 0; m < RPT; ++m)
-        s[m] = *reinterpret_cast<const f32x4_t *>(S + (int64_t)(rg + RG * m) * D + 4 * c4);
+        s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(S + (int64_t)(rg + RG * m) * D + 4 * c4));
     __syncthreads();
     f32x4_t acc = zero4();
 #pragma unroll
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const T *__restrict__ q,
             acc[x] += qa * s[m][x];           // o uses the state before the update
             s[m][x] += ka * vv[x];
         }
-        *reinterpret_cast<f32x4_t *>(S + (int64_t)a * D + 4 * c4) = s[m];
+        __builtin_nontemporal_store(s[m], reinterpret_cast<f32x4_t *>(S + (int64_t)a * D + 4 * c4));
     }
     red[rg][c4] = acc;
     __syncthreads();
