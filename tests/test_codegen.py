@@ -6,6 +6,10 @@ hipcc cross-compiles to assembly).
   between; a missing one made a buffer store pick up new values in some
   lanes).
 * The bf16 prefill kernels must not spill to scratch memory.
+* Inside the fused kernel's tile loop the compiler must not wait for every
+  outstanding vector-memory load (vmcnt(0)) before an LDS read: it does so
+  when it loses the alias information that ties an LDS read to one ring
+  stage, which stalls the buffer-to-LDS prefetch of the following tiles.
 """
 import os
 import re
@@ -78,3 +82,23 @@ def test_bf16_prefill_kernels_do_not_spill(tmp_path):
         j = text.index(".Lfunc_end", i)
         body = text[i:j]
         assert "scratch_" not in body, k
+
+
+def _kernel_bodies(text, pattern):
+    for k in re.findall(pattern, text, re.M):
+        i = text.index(k + ":")
+        j = text.index(".Lfunc_end", i)
+        yield k, text[i:j]
+
+
+def test_fused_kernel_keeps_prefetch_in_flight(tmp_path):
+    text = _asm(os.path.join(CSRC, "la_prefill.hip"), tmp_path)
+    found = False
+    for k, body in _kernel_bodies(text, r"^(_ZN2la11k_fused_dma\w+):"):
+        found = True
+        insts = list(_instructions(body))
+        # the prologue waits once for the chunk's start state; the end of the
+        # kernel waits for everything; nothing else may drain the queue
+        full = [s for s in insts if re.fullmatch(r"s_waitcnt vmcnt\(0\)", s)]
+        assert len(full) <= 1, (k, len(full))
+    assert found
