@@ -731,6 +731,21 @@ __global__ __launch_bounds__(512, 2) void k_summary_dma(KParams p) {
                 dst[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c] = S[ia][ib][r];
 }
 
+// The K/V ring: one LDS array per stage, so the compiler tracks each
+// buffer-to-LDS load by its destination stage.
+template <int NST, int SBY>
+struct Ring;
+template <int SBY>
+struct Ring<4, SBY> {
+    __device__ __forceinline__ static void get(char *(&s)[4]) {
+        __shared__ __attribute__((aligned(16))) char s0[SBY];
+        __shared__ __attribute__((aligned(16))) char s1[SBY];
+        __shared__ __attribute__((aligned(16))) char s2[SBY];
+        __shared__ __attribute__((aligned(16))) char s3[SBY];
+        s[0] = s0; s[1] = s1; s[2] = s2; s[3] = s3;
+    }
+};
+
 // Which 32-element groups [lo(jt), hi(jt)) of the next block's Q a wave
 // requests in tile jt of a block with TPB tiles (none in the last tile), and
 // how many loads that is (n(-1) = 0: the tile before a block's first).
@@ -748,9 +763,12 @@ struct QSplit {
 // Per chunk: walk the blocks carrying S; per block O^T = S^T Q^T + V^T P^T
 // with P = mask(Q K^T), then S += K^T V.
 //
-// K and V stream through a 4-stage LDS ring in 64-token tiles, loaded by
-// buffer loads straight into LDS; tile t + 3 is requested while tile t is
-// used.  The four tiles of a ring cycle (a "super-block" of 256 tokens, one
+// K and V stream through a 4-stage LDS ring in TJ = 64-token tiles, loaded
+// by buffer loads straight into LDS; tile t + LA (LA = 2) is requested while
+// tile t is used.  Two tiles in flight per CU (64 KiB) already reach the
+// bandwidth that three do with the products left out, and with them the
+// whole kernel is about 1% faster (the fourth stage holds the tile before).
+// The four tiles of a ring cycle (a "super-block" of 256 tokens, one
 // or more whole blocks) are separate compile-time copies of the tile body, so
 // a tile's stage, its place in its block and its wait counts are constants.
 // All global accesses go through buffer resources that end at the chunk end:
@@ -768,24 +786,23 @@ struct QSplit {
 // it needs:
 //   the next block's Q is loaded over the block's tiles, each part at the
 //   top of a tile ahead of its DMA;
-//   tile not ending a block: DMA(t+3) at its top; at its end DMA(t+1) must
-//   have landed; younger are DMA(t+2), DMA(t+3) and the Q loads of this
-//   tile and the one before;
+//   tile not ending a block: DMA(t+LA) at its top; at its end DMA(t+1) must
+//   have landed; younger are DMA(t+2 .. t+LA) and the Q loads of the LA-1
+//   tiles up to this one;
 //   tile ending a block: all of the next Q and DMA(t+1) must have landed;
-//   younger is the DMA of the tile before; then it requests DMA(t+3);
+//   younger is DMA(t+2 .. t+LA-1); then it requests DMA(t+LA);
 //   a wave stores its O after the wait of the last tile that holds keys of
 //   its rows (O is final there), so the stores spread over the block and
 //   complete during the following tile.
 // With one tile per block the next Q is loaded after the tile's scores and
 // the tile waits for every load.
-template <int D, int BLK, int NW>
+template <int D, int BLK, int NW, int TJ, int NST, int LA>
 __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     using T = bf16_t;
     using C = Cfg<T, D, BLK, NW>;
-    constexpr int TJ = C::TJ;
     using LT = SubRows<TJ>;                          // K / V tiles
     using LS = SubRows<D>;                           // state copy S^T (rows = value dim)
-    constexpr int NST = 4;                           // ring stages = tiles per super-block
+    static_assert(LA >= 1 && LA < NST, "tiles requested ahead of the one in use");
     constexpr int TPB = BLK / TJ;                    // tiles per block
     constexpr int RB = D * 2;                        // bytes per token row
     constexpr int TB = TJ * RB;                      // bytes of one tensor tile
@@ -800,12 +817,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     using QS = QSplit<TPB, C::KC, C::NSW>;
     static_assert(NST % TPB == 0 && (2 * NI) % NW == 0 && TB % 1024 == 0, "tile split");
     static_assert(C::NCT % 2 == 0, "column tiles are stored in pairs");
-    __shared__ __attribute__((aligned(16))) char stage0[SBY];
-    __shared__ __attribute__((aligned(16))) char stage1[SBY];
-    __shared__ __attribute__((aligned(16))) char stage2[SBY];
-    __shared__ __attribute__((aligned(16))) char stage3[SBY];
     __shared__ __attribute__((aligned(16))) char st[C::ST_BYTES];
-    char *const stages[NST] = {stage0, stage1, stage2, stage3};
+    char *stages[NST];
+    Ring<NST, SBY>::get(stages);
 
     const int h = blockIdx.y;
     const int gch = blockIdx.x;
@@ -902,13 +916,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
                            u32x2_t{pack_bf16x2(Sx[ia][ib][0], Sx[ia][ib][1]), pack_bf16x2(Sx[ia][ib][2], Sx[ia][ib][3])});
     };
 
-    // ---- prologue: the first block's Q, tiles 0 and 1, the state at the
-    // chunk start (exclusive prefix from the scan; zero for a sequence's
-    // first chunk); tile 2 stays in flight
+    // ---- prologue: the first block's Q, tile 0 (and tile 1 when three are
+    // kept in flight), the state at the chunk start (exclusive prefix from
+    // the scan; zero for a sequence's first chunk); tile LA - 1 stays in flight
     f32x4_t S[C::SA][C::SB];
     load_q(Q, 0, 0, C::KC);
     issue(0, stages[0]);
-    issue(1, stages[1]);
+    if constexpr (LA >= 3) issue(1, stages[1]);
     {
         const float *src = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
         const bool first = cl == 0;
@@ -922,7 +936,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         write_state(S);
     }
     wait_vm_lgkm0<0>();
-    issue(2, stages[2]);
+    if constexpr (LA >= 2) issue(LA - 1, stages[LA - 1]);
     wg_barrier();
 
     f32x4_t O[C::NSW][C::NCT];
@@ -953,6 +967,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
 
     auto tile = [&](auto J_c, int sb) {
         constexpr int J = decltype(J_c)::value;     // tile within the super-block = ring stage
+        static_assert(J < NST, "one tile per ring stage");
         constexpr int jt = J % TPB;                  // tile within its block
         constexpr bool first = jt == 0, last = jt == TPB - 1;
         const int t = sb * NST + J;
@@ -960,7 +975,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         const int tb = bi * BLK;                     // block's first token (chunk-relative)
         const bool more = bi + 1 < nblk;
         if constexpr (QS::n(jt) > 0) load_q(Qn, tb + BLK, QS::lo(jt), QS::hi(jt));
-        if constexpr (!last) issue(t + 3, stages[(J + 3) % NST]);
+        // DMA(t + LA) at the top of the tile (with two or more tiles in
+        // flight a block's last tile requests it after its wait instead)
+        if constexpr (!last || LA == 1) issue(t + LA, stages[(J + LA) % NST]);
         const char *stage = stages[J];
         const char *krow = stage + row8;             // K rows (b128 reads)
         const char *vcol = stage + vpv_off;          // V columns of tile ct0 (tr reads)
@@ -1076,26 +1093,30 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
                 }
                 write_state(S);
             }
+            // the next block's Q and DMA(t+1) have landed; younger is
+            // DMA(t+2 .. t+LA-1) (with one tile per block Q itself was
+            // reloaded in this tile and everything is waited for)
             if constexpr (TPB == 1) {
                 wait_vm_lgkm0<0>();
             } else {
-                wait_vm_lgkm0<IPW>();                // the next Q and DMA(t+1) have landed
+                wait_vm_lgkm0<(LA >= 2 ? (LA - 2) * IPW : 0)>();
 #pragma unroll
                 for (int si = 0; si < C::NSW; ++si)
 #pragma unroll
                     for (int kc = 0; kc < C::KC; ++kc) Q[si][kc] = Qn[si][kc];
             }
-            issue(t + 3, stages[(J + 3) % NST]);
+            if constexpr (LA > 1) issue(t + LA, stages[(J + LA) % NST]);
         } else {
             if (more) state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
-            // DMA(t+1) has landed; younger are two tiles of DMA and the Q
-            // loads of this tile and the one before
-            wait_vm_lgkm0<2 * IPW + QS::n(jt) + QS::n(jt - 1)>();
+            // DMA(t+1) has landed; younger are DMA(t+2 .. t+LA) and the Q
+            // loads of the LA-1 tiles up to this one
+            wait_vm_lgkm0<(LA - 1) * IPW + (LA >= 2 ? QS::n(jt) : 0) + (LA >= 3 ? QS::n(jt - 1) : 0)>();
         }
         if (jt == jl) store_o(bi);
         wg_barrier();
     };
 
+    static_assert(NST == 4, "ring stages");
     for (int sb = 0; sb < nsb; ++sb) {
         tile(integral_constant<int, 0>{}, sb);
         tile(integral_constant<int, 1>{}, sb);
@@ -1141,7 +1162,7 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
     if constexpr (sizeof(T) == 2)
         {
         constexpr int NWF = fused_waves(D, BLK);
-        hipLaunchKernelGGL((k_fused_dma<D, BLK, NWF>), gchunks, dim3(NWF * 64), 0, st, kp);
+        hipLaunchKernelGGL((k_fused_dma<D, BLK, NWF, 64, 4, 2>), gchunks, dim3(NWF * 64), 0, st, kp);
     }
     else
         hipLaunchKernelGGL((k_fused<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
