@@ -633,25 +633,49 @@ __device__ __forceinline__ uint32_t col_tile_off(int l, int ct) {
     return SubRows<ROWS>::col_base(l, ct & 1) + (ct >> 1) * SubRows<ROWS>::BLOCK;
 }
 
+// The K/V ring: one LDS array per stage, so the compiler tracks each
+// buffer-to-LDS load by its destination stage.
+template <int NST, int SBY>
+struct Ring;
+template <int SBY>
+struct Ring<4, SBY> {
+    __device__ __forceinline__ static void get(char *(&s)[4]) {
+        __shared__ __attribute__((aligned(16))) char s0[SBY];
+        __shared__ __attribute__((aligned(16))) char s1[SBY];
+        __shared__ __attribute__((aligned(16))) char s2[SBY];
+        __shared__ __attribute__((aligned(16))) char s3[SBY];
+        s[0] = s0; s[1] = s1; s[2] = s2; s[3] = s3;
+    }
+};
+
+template <int SBY>
+struct Ring<2, SBY> {
+    __device__ __forceinline__ static void get(char *(&s)[2]) {
+        __shared__ __attribute__((aligned(16))) char s0[SBY];
+        __shared__ __attribute__((aligned(16))) char s1[SBY];
+        s[0] = s0; s[1] = s1;
+    }
+};
+
 // U_c = K_c^T V_c over a chunk.  K/V tiles of 64 tokens are buffer-loaded
-// straight into a two-stage LDS ring (two workgroups fit per CU); the buffer
-// resources end at the chunk end, so rows past it load as zeros.  The stages
-// are separate LDS arrays so the compiler tracks each DMA by destination.
-template <int D, int BLK>
-__global__ __launch_bounds__(512, 2) void k_summary_dma(KParams p) {
-    using C = Cfg<bf16_t, D, BLK>;
+// straight into an NST-stage LDS ring, LA tiles ahead of the one in use (one
+// barrier per tile); the buffer resources end at the chunk end, so rows past
+// it load as zeros.  The stages are separate LDS arrays so the compiler
+// tracks each DMA by destination.
+template <int D, int BLK, int NW, int NST, int LA>
+__global__ __launch_bounds__(NW * 64, 1024 / (NW * 64)) void k_summary_dma(KParams p) {
+    using C = Cfg<bf16_t, D, BLK, NW>;
     constexpr int TJ = C::TJ;
     using LT = SubRows<TJ>;
-    constexpr int NW = 8;
     constexpr int RB = D * 2;                        // bytes per token row
     constexpr int TB = TJ * RB;                      // bytes of one tensor tile
     constexpr int SBY = 2 * TB;                      // stage: K tile then V tile
     constexpr int NI = TB / 1024;                    // 1 KiB DMA instructions per tensor tile
     constexpr int IPW = 2 * NI / NW;                 // per wave per tile
     static_assert((2 * NI) % NW == 0 && TB % 1024 == 0, "tile split");
-    __shared__ __attribute__((aligned(16))) char stage0[SBY];
-    __shared__ __attribute__((aligned(16))) char stage1[SBY];
-    char *const stages[2] = {stage0, stage1};
+    static_assert(LA >= 1 && LA < NST && (NST == 2 || NST == 4), "ring");
+    char *stages[NST];
+    Ring<NST, SBY>::get(stages);
     const int h = blockIdx.y;
     const int gch = blockIdx.x;
     if (gch >= p.chunk_off[p.nseq]) return;
@@ -701,24 +725,40 @@ __global__ __launch_bounds__(512, 2) void k_summary_dma(KParams p) {
         for (int ib = 0; ib < C::SB; ++ib) S[ia][ib] = zero4();
 
     const int ntile = (n + TJ - 1) / TJ;
-    auto step = [&](int it, char *cur, char *nxt) {
-        issue(it + 1, nxt);                          // past the end: zeros, never read
-        wait_vm_lgkm0<IPW>();                        // tile it has landed
+    // Tile t of a ring cycle: request tile t + LA into the stage freed by
+    // the last barrier (past the end: zeros, never read), add tile t, wait
+    // until tile t + 1 has landed (younger: tiles t + 2 .. t + LA) and
+    // publish it with the barrier.
+    auto tile = [&](auto J_c, int sb) {
+        constexpr int J = decltype(J_c)::value;
+        static_assert(J < NST, "one tile per ring stage");
+        const int t = sb * NST + J;
+        issue(t + LA, stages[(J + LA) % NST]);
+        if (t < ntile) {
+            const char *ka[C::SA];
+            const char *vb[C::SB];
+#pragma unroll
+            for (int ia = 0; ia < C::SA; ++ia) ka[ia] = stages[J] + ka_off[ia];
+#pragma unroll
+            for (int ib = 0; ib < C::SB; ++ib) vb[ib] = stages[J] + vb_off[ib];
+            state_update_tr<TJ, C::SA, C::SB>(S, ka, vb);
+        }
+        wait_vm_lgkm0<(LA - 1) * IPW>();
         wg_barrier();
-        const char *ka[C::SA];
-        const char *vb[C::SB];
-#pragma unroll
-        for (int ia = 0; ia < C::SA; ++ia) ka[ia] = cur + ka_off[ia];
-#pragma unroll
-        for (int ib = 0; ib < C::SB; ++ib) vb[ib] = cur + vb_off[ib];
-        state_update_tr<TJ, C::SA, C::SB>(S, ka, vb);
-        wait_vm_lgkm0<IPW>();                        // own LDS reads done (the next DMA may stay)
-        wg_barrier();                                // nobody reads `cur` any more: it may be refilled
     };
-    issue(0, stages[0]);
-    for (int it = 0; it < ntile; it += 2) {
-        step(it, stages[0], stages[1]);
-        if (it + 1 < ntile) step(it + 1, stages[1], stages[0]);
+#pragma unroll
+    for (int i = 0; i < LA; ++i) issue(i, stages[i]);
+    wait_vm_lgkm0<(LA - 1) * IPW>();                 // tile 0 has landed
+    wg_barrier();
+    using std::integral_constant;
+    const int nsb = (ntile + NST - 1) / NST;
+    for (int sb = 0; sb < nsb; ++sb) {
+        tile(integral_constant<int, 0>{}, sb);
+        tile(integral_constant<int, 1>{}, sb);
+        if constexpr (NST == 4) {
+            tile(integral_constant<int, 2>{}, sb);
+            tile(integral_constant<int, 3>{}, sb);
+        }
     }
     wait_vm_lgkm0<0>();                              // the DMA past the end has landed
     float *dst = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
@@ -730,21 +770,6 @@ __global__ __launch_bounds__(512, 2) void k_summary_dma(KParams p) {
             for (int r = 0; r < 4; ++r)
                 dst[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c] = S[ia][ib][r];
 }
-
-// The K/V ring: one LDS array per stage, so the compiler tracks each
-// buffer-to-LDS load by its destination stage.
-template <int NST, int SBY>
-struct Ring;
-template <int SBY>
-struct Ring<4, SBY> {
-    __device__ __forceinline__ static void get(char *(&s)[4]) {
-        __shared__ __attribute__((aligned(16))) char s0[SBY];
-        __shared__ __attribute__((aligned(16))) char s1[SBY];
-        __shared__ __attribute__((aligned(16))) char s2[SBY];
-        __shared__ __attribute__((aligned(16))) char s3[SBY];
-        s[0] = s0; s[1] = s1; s[2] = s2; s[3] = s3;
-    }
-};
 
 // Which 32-element groups [lo(jt), hi(jt)) of the next block's Q a wave
 // requests in tile jt of a block with TPB tiles (none in the last tile), and
@@ -1128,6 +1153,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
 
 // -------------------------------------------------------------- host side
 
+// Chunk summary kernel: waves per workgroup, ring stages and tiles in flight.
+constexpr int kSumWaves = 8, kSumStages = 2, kSumAhead = 1;
+
 // Waves per workgroup of the bf16 fused kernel.
 constexpr int fused_waves(int D, int BLK) { return (D == 128 && BLK == 256) ? 16 : 8; }
 
@@ -1144,7 +1172,8 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
     // the chunk summaries before it; with one chunk per sequence there is none.
     if (!plan.single_chunk) {
         if constexpr (sizeof(T) == 2)
-            hipLaunchKernelGGL((k_summary_dma<D, BLK>), gchunks, dim3(512), 0, st, kp);
+            hipLaunchKernelGGL((k_summary_dma<D, BLK, kSumWaves, kSumStages, kSumAhead>), gchunks,
+                               dim3(kSumWaves * 64), 0, st, kp);
         else
             hipLaunchKernelGGL((k_summary<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
     }
