@@ -258,8 +258,12 @@ def cpu_baseline(w, target_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # The GPU's clocks take tens of milliseconds of sustained load to settle:
+    # with a few warm-up steps the first timed steps run measurably slower
+    # (about 7% on the MiniMax layer), so the default warm-up is 100 steps
+    # (about 45 ms) before 50 timed ones.
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-extras", action="store_true", help="only the headline prefill workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -326,13 +330,13 @@ def main():
     if not args.no_extras:
         wd = synth.WORKLOADS["decode256"]
         log(f"decode {wd.name}: {wd.note}")
-        dms, dgbs, dtok = bench_decode(wd, 3, dev)
+        dms, dgbs, dtok = bench_decode(wd, 5, dev)
         out["decode"] = {"workload": wd.note, "ms_per_step": dms, "gbs": dgbs,
                          "hbm_frac": dgbs / PEAK_HBM_GBS, "head_steps_per_s": dtok}
         log(json.dumps(out["decode"]))
         wl = synth.WORKLOADS["long_1m"]
         log(f"prefill {wl.name}: {wl.note}")
-        lms, lstage, lchunk, _ = bench_prefill(wl, 3, 1, dev)
+        lms, lstage, lchunk, _ = bench_prefill(wl, 5, 3, dev)
         lht = wl.batch * wl.heads * wl.seq_len
         lbytes = lht * 4 * wl.head_dim * 2
         out["long_1m"] = {"workload": wl.note, "ms_per_step": lms,
