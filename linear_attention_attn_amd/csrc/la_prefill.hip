@@ -657,25 +657,28 @@ struct Ring<2, SBY> {
     }
 };
 
-// U_c = K_c^T V_c over a chunk.  K/V tiles of 64 tokens are buffer-loaded
-// straight into an NST-stage LDS ring, LA tiles ahead of the one in use (one
-// barrier per tile); the buffer resources end at the chunk end, so rows past
-// it load as zeros.  The stages are separate LDS arrays so the compiler
-// tracks each DMA by destination.
-template <int D, int BLK, int NW, int NST, int LA>
-__global__ __launch_bounds__(NW * 64, 1024 / (NW * 64)) void k_summary_dma(KParams p) {
+
+// U_c = K_c^T V_c over a chunk, with the K/V tiles staged through
+// registers: each wave loads its 16-byte pieces of tile t + 2 into registers
+// (buffer loads, rows past the chunk end read as zeros) while tile t is
+// summed, and writes tile t + 1 into the other LDS stage at the end of tile
+// t.  Same LDS layout as the fused kernel's tiles.  Measured on MI355X,
+// buffer-to-LDS loads alone stream at most ~6.3 TB/s and register loads
+// ~7.3 TB/s; this kernel does little besides streaming, and staging through
+// registers made it a little faster (about 1% on the 1M-token workload).
+template <int D, int BLK, int NW>
+__global__ __launch_bounds__(NW * 64, 1024 / (NW * 64)) void k_summary_reg(KParams p) {
     using C = Cfg<bf16_t, D, BLK, NW>;
     constexpr int TJ = C::TJ;
     using LT = SubRows<TJ>;
     constexpr int RB = D * 2;                        // bytes per token row
     constexpr int TB = TJ * RB;                      // bytes of one tensor tile
     constexpr int SBY = 2 * TB;                      // stage: K tile then V tile
-    constexpr int NI = TB / 1024;                    // 1 KiB DMA instructions per tensor tile
-    constexpr int IPW = 2 * NI / NW;                 // per wave per tile
+    constexpr int NI = TB / 1024;                    // 1 KiB pieces per tensor tile
+    constexpr int IPW = 2 * NI / NW;                 // pieces per wave per tile
     static_assert((2 * NI) % NW == 0 && TB % 1024 == 0, "tile split");
-    static_assert(LA >= 1 && LA < NST && (NST == 2 || NST == 4), "ring");
-    char *stages[NST];
-    Ring<NST, SBY>::get(stages);
+    char *stages[2];
+    Ring<2, SBY>::get(stages);
     const int h = blockIdx.y;
     const int gch = blockIdx.x;
     if (gch >= p.chunk_off[p.nseq]) return;
@@ -698,8 +701,9 @@ __global__ __launch_bounds__(NW * 64, 1024 / (NW * 64)) void k_summary_dma(KPara
 #pragma unroll
     for (int ib = 0; ib < C::SB; ++ib) vb_off[ib] = TB + col_tile_off<TJ>(l, b0 + ib);
 
-    // DMA: wave instruction gi = w * IPW + ii fills 16 rows of one 32-element
-    // column block of the K (gi < NI) or V tile (as in the fused kernel)
+    // piece gi = w * IPW + ii: 16 rows of one 32-element column block of the
+    // K (gi < NI) or V tile; lane l brings row row0 + l / 4, physical 16-byte
+    // chunk l % 4, and writes it at LDS byte dlo + 16 l of the stage
     uint32_t dvo[IPW], dlo[IPW];
     __amdgpu_buffer_rsrc_t drs[IPW];
 #pragma unroll
@@ -710,12 +714,18 @@ __global__ __launch_bounds__(NW * 64, 1024 / (NW * 64)) void k_summary_dma(KPara
         const int blk = x / (TJ / 16), row0 = 16 * (x % (TJ / 16));
         const int row = row0 + (l >> 2);
         dvo[ii] = (uint32_t)(row * RB + blk * 64 + (((l & 3) ^ LT::swz(row)) << 4));
-        dlo[ii] = (isv ? TB : 0) + blk * LT::BLOCK + row0 * 64;
+        dlo[ii] = (isv ? TB : 0) + blk * LT::BLOCK + row0 * 64 + 16 * l;
         drs[ii] = isv ? rv : rk;
     }
-    auto issue = [&](int tile, char *stage) {
+    u32x4_t R0[IPW], R1[IPW];
+    auto load = [&](int tile, u32x4_t (&R)[IPW]) {
 #pragma unroll
-        for (int ii = 0; ii < IPW; ++ii) dma_lds16(drs[ii], stage + dlo[ii], dvo[ii], (uint32_t)(tile * TB));
+        for (int ii = 0; ii < IPW; ++ii)
+            R[ii] = __builtin_amdgcn_raw_buffer_load_b128(drs[ii], (int)dvo[ii], tile * TB, 0);
+    };
+    auto put = [&](char *stage, const u32x4_t (&R)[IPW]) {
+#pragma unroll
+        for (int ii = 0; ii < IPW; ++ii) *reinterpret_cast<u32x4_t *>(stage + dlo[ii]) = R[ii];
     };
 
     f32x4_t S[C::SA][C::SB];
@@ -723,44 +733,37 @@ __global__ __launch_bounds__(NW * 64, 1024 / (NW * 64)) void k_summary_dma(KPara
     for (int ia = 0; ia < C::SA; ++ia)
 #pragma unroll
         for (int ib = 0; ib < C::SB; ++ib) S[ia][ib] = zero4();
+    auto sum_tile = [&](const char *stage) {
+        const char *ka[C::SA];
+        const char *vb[C::SB];
+#pragma unroll
+        for (int ia = 0; ia < C::SA; ++ia) ka[ia] = stage + ka_off[ia];
+#pragma unroll
+        for (int ib = 0; ib < C::SB; ++ib) vb[ib] = stage + vb_off[ib];
+        state_update_tr<TJ, C::SA, C::SB>(S, ka, vb);
+    };
 
     const int ntile = (n + TJ - 1) / TJ;
-    // Tile t of a ring cycle: request tile t + LA into the stage freed by
-    // the last barrier (past the end: zeros, never read), add tile t, wait
-    // until tile t + 1 has landed (younger: tiles t + 2 .. t + LA) and
-    // publish it with the barrier.
-    auto tile = [&](auto J_c, int sb) {
-        constexpr int J = decltype(J_c)::value;
-        static_assert(J < NST, "one tile per ring stage");
-        const int t = sb * NST + J;
-        issue(t + LA, stages[(J + LA) % NST]);
-        if (t < ntile) {
-            const char *ka[C::SA];
-            const char *vb[C::SB];
-#pragma unroll
-            for (int ia = 0; ia < C::SA; ++ia) ka[ia] = stages[J] + ka_off[ia];
-#pragma unroll
-            for (int ib = 0; ib < C::SB; ++ib) vb[ib] = stages[J] + vb_off[ib];
-            state_update_tr<TJ, C::SA, C::SB>(S, ka, vb);
-        }
-        wait_vm_lgkm0<(LA - 1) * IPW>();
-        wg_barrier();
-    };
-#pragma unroll
-    for (int i = 0; i < LA; ++i) issue(i, stages[i]);
-    wait_vm_lgkm0<(LA - 1) * IPW>();                 // tile 0 has landed
+    load(0, R0);
+    load(1, R1);
+    put(stages[0], R0);
+    wait_vm_lgkm0<63>();                             // own LDS writes done
     wg_barrier();
-    using std::integral_constant;
-    const int nsb = (ntile + NST - 1) / NST;
-    for (int sb = 0; sb < nsb; ++sb) {
-        tile(integral_constant<int, 0>{}, sb);
-        tile(integral_constant<int, 1>{}, sb);
-        if constexpr (NST == 4) {
-            tile(integral_constant<int, 2>{}, sb);
-            tile(integral_constant<int, 3>{}, sb);
+    for (int t = 0; t < ntile; t += 2) {
+        load(t + 2, R0);                             // past the end: zeros, never used
+        sum_tile(stages[0]);
+        put(stages[1], R1);                          // tile t + 1 (stage 1 was last read in tile t - 1)
+        wait_vm_lgkm0<63>();
+        wg_barrier();
+        if (t + 1 < ntile) {
+            load(t + 3, R1);
+            sum_tile(stages[1]);
+            put(stages[0], R0);                      // tile t + 2
+            wait_vm_lgkm0<63>();
+            wg_barrier();
         }
     }
-    wait_vm_lgkm0<0>();                              // the DMA past the end has landed
+    wait_vm_lgkm0<0>();
     float *dst = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
 #pragma unroll
     for (int ia = 0; ia < C::SA; ++ia)
@@ -1153,9 +1156,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
 
 // -------------------------------------------------------------- host side
 
-// Chunk summary kernel: waves per workgroup, ring stages and tiles in flight.
-constexpr int kSumWaves = 8, kSumStages = 2, kSumAhead = 1;
-
 // Waves per workgroup of the bf16 fused kernel.
 constexpr int fused_waves(int D, int BLK) { return (D == 128 && BLK == 256) ? 16 : 8; }
 
@@ -1172,8 +1172,7 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
     // the chunk summaries before it; with one chunk per sequence there is none.
     if (!plan.single_chunk) {
         if constexpr (sizeof(T) == 2)
-            hipLaunchKernelGGL((k_summary_dma<D, BLK, kSumWaves, kSumStages, kSumAhead>), gchunks,
-                               dim3(kSumWaves * 64), 0, st, kp);
+            hipLaunchKernelGGL((k_summary_reg<D, BLK, 8>), gchunks, dim3(512), 0, st, kp);
         else
             hipLaunchKernelGGL((k_summary<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
     }

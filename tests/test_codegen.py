@@ -75,7 +75,7 @@ def test_hazard_scan_catches_pattern():
 
 def test_bf16_prefill_kernels_do_not_spill(tmp_path):
     text = _asm(os.path.join(CSRC, "la_prefill.hip"), tmp_path)
-    kernels = re.findall(r"^(_ZN2la1\dk_(?:fused|summary)_dma\w+):", text, re.M)
+    kernels = re.findall(r"^(_ZN2la1\dk_(?:fused_dma|summary_reg)\w+):", text, re.M)
     assert kernels
     for k in kernels:
         i = text.index(k + ":")
