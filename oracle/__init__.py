@@ -66,9 +66,13 @@ def _load():
     lib.lao_varlen.argtypes = [f32p, f32p, f32p, f64p, c_int, i64, i32p, c_int, c_int,
                                c_int, i64, c_int]
     lib.lao_decode_units.argtypes = [f32p, f32p, f32p, f64p, f64p, i64, i64, c_int, c_int]
+    lib.lao_units_state.argtypes = [f32p, f32p, f32p, f64p, i64, i64, c_int, f64p, f64p, c_int]
+    lib.lao_varlen_state.argtypes = [f32p, f32p, f32p, f64p, c_int, i64, i32p, c_int, c_int,
+                                     f64p, f64p, c_int]
     lib.lao_max_threads.restype = c_int
     for fn in ("lao_naive", "lao_recurrent", "lao_recurrent_rows", "lao_block",
-               "lao_decode_step", "lao_units", "lao_varlen", "lao_decode_units"):
+               "lao_decode_step", "lao_units", "lao_varlen", "lao_decode_units",
+               "lao_units_state", "lao_varlen_state"):
         getattr(lib, fn).restype = None
     _lib = lib
     return lib
@@ -130,6 +134,47 @@ def causal_linear_attention_varlen(q, k, v, cu_seqlens, form: str = "recurrent",
                    _p(o, ctypes.c_double), heads, T, _p(cu, ctypes.c_int32), len(cu) - 1,
                    d, FORMS[form], int(block_size), int(nthreads))
     return o
+
+
+def causal_linear_attention_state(q, k, v, S0=None, nthreads: int = 0):
+    """(o, S_final) for inputs [..., n, d] (every leading index a unit), each
+    unit starting from S0[...] ([..., d, d]; None = zero).  Recurrent form:
+    o_t = q_t (S0 + sum_{j<=t} k_j^T v_j), S_final = S0 + K^T V.  float64."""
+    lib = _load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    assert q.shape == k.shape == v.shape and q.ndim >= 2
+    n, d = q.shape[-2], q.shape[-1]
+    lead = q.shape[:-2]
+    units = int(np.prod(lead)) if lead else 1
+    o = np.zeros(q.shape, dtype=np.float64)
+    Sf = np.zeros(lead + (d, d), dtype=np.float64)
+    s0 = None if S0 is None else np.ascontiguousarray(np.asarray(S0, np.float64).reshape(lead + (d, d)))
+    if units == 0:
+        return o, Sf
+    lib.lao_units_state(_p(q, ctypes.c_float), _p(k, ctypes.c_float), _p(v, ctypes.c_float),
+                        _p(o, ctypes.c_double), units, n, d,
+                        None if s0 is None else _p(s0, ctypes.c_double), _p(Sf, ctypes.c_double),
+                        int(nthreads))
+    return o, Sf
+
+
+def causal_linear_attention_varlen_state(q, k, v, cu_seqlens, S0=None, nthreads: int = 0):
+    """(o, S_final) for packed input [heads, T, d] with per-sequence states
+    S0 / S_final laid out [nseq, heads, d, d] (S0 None = zero)."""
+    lib = _load()
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens), dtype=np.int32)
+    heads, T, d = q.shape
+    nseq = len(cu) - 1
+    assert cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+    o = np.zeros(q.shape, dtype=np.float64)
+    Sf = np.zeros((nseq, heads, d, d), dtype=np.float64)
+    s0 = None if S0 is None else np.ascontiguousarray(np.asarray(S0, np.float64).reshape(nseq, heads, d, d))
+    lib.lao_varlen_state(_p(q, ctypes.c_float), _p(k, ctypes.c_float), _p(v, ctypes.c_float),
+                         _p(o, ctypes.c_double), heads, T, _p(cu, ctypes.c_int32), nseq, d,
+                         None if s0 is None else _p(s0, ctypes.c_double), _p(Sf, ctypes.c_double),
+                         int(nthreads))
+    return o, Sf
 
 
 def recurrent_rows(q, k, v, rows) -> np.ndarray:

@@ -247,6 +247,54 @@ void lao_varlen(const float *q, const float *k, const float *v, double *o,
     }
 }
 
+/* Recurrent form over `units` independent [n][d] streams ([units][n][d]),
+ * each starting from its own state: S0 [units][d][d] (NULL = zero) and
+ * ending with its final state written to Sf [units][d][d] (NULL = not
+ * wanted).  o_t = q_t (S0 + sum_{j<=t} k_j^T v_j), S_final = S0 + sum k^T v.
+ * This is the state a prefill hands to decoding, or to the next piece of a
+ * sequence prefilled in pieces ([W] "Lightning Attention 设计": the KV state
+ * carries everything earlier tokens contribute). */
+void lao_units_state(const float *q, const float *k, const float *v, double *o,
+                     int64_t units, int64_t n, int d, const double *S0, double *Sf,
+                     int nthreads)
+{
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t u = 0; u < units; ++u) {
+        size_t off = (size_t)u * (size_t)n * (size_t)d, dd = (size_t)d * d;
+        double *S = (double *)malloc(dd * sizeof(double));
+        for (size_t e = 0; e < dd; ++e) S[e] = S0 ? S0[(size_t)u * dd + e] : 0.0;
+        lao_recurrent(q + off, k + off, v + off, o + off, n, d, S);
+        if (Sf)
+            for (size_t e = 0; e < dd; ++e) Sf[(size_t)u * dd + e] = S[e];
+        free(S);
+    }
+}
+
+/* Packed input as in lao_varlen, recurrent form, with per-sequence states
+ * S0 / Sf laid out [nseq][heads][d][d] (NULL as in lao_units_state).  A
+ * sequence of length 0 ends in its initial state. */
+void lao_varlen_state(const float *q, const float *k, const float *v, double *o,
+                      int heads, int64_t T, const int32_t *cu, int nseq, int d,
+                      const double *S0, double *Sf, int nthreads)
+{
+    set_threads(nthreads);
+    int64_t total = (int64_t)heads * nseq;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t x = 0; x < total; ++x) {
+        int h = (int)(x / nseq), s = (int)(x % nseq);
+        int64_t n = (int64_t)cu[s + 1] - cu[s];
+        size_t off = ((size_t)h * (size_t)T + (size_t)cu[s]) * (size_t)d, dd = (size_t)d * d;
+        size_t so = ((size_t)s * heads + h) * dd;
+        double *S = (double *)malloc(dd * sizeof(double));
+        for (size_t e = 0; e < dd; ++e) S[e] = S0 ? S0[so + e] : 0.0;
+        if (n > 0) lao_recurrent(q + off, k + off, v + off, o + off, n, d, S);
+        if (Sf)
+            for (size_t e = 0; e < dd; ++e) Sf[so + e] = S[e];
+        free(S);
+    }
+}
+
 /* `steps` decode steps over `units` independent states.
  * q, k, v: [steps][units][d]; S: [units][d][d] (in/out); o: [steps][units][d]. */
 void lao_decode_units(const float *q, const float *k, const float *v,

@@ -11,6 +11,7 @@ Implementation signatures:
     blk(q, k, v, B) -> o                 block form with block size B
     dec(q, k, v, S0) -> (o, S_final)     q, k, v: [steps, units, d], S0 [units, d, d]
     varlen(q, k, v, cu) -> o             q, k, v: [heads, T, d]
+    stf(q, k, v, S0) -> (o, S_final)     one [n, d] unit continued from S0 [d, d]
 """
 import json
 import os
@@ -179,3 +180,59 @@ def check_linearity(fwd, n=30, d=5, seed=19):
     o = np.asarray(fwd(q, k, v1))
     assert np.array_equal(np.asarray(fwd(2 * q, k, v1)), 2 * o)
     assert np.array_equal(np.asarray(fwd(q, k, v1 + v2)), o + np.asarray(fwd(q, k, v2)))
+
+
+# ---- state handoff: a unit continued from an initial state S0 -------------
+
+def check_golden_state(stf):
+    """Hand-worked continuation from a non-symmetric S0 (tests/golden)."""
+    g = load_golden("hand_state_d2_n2.json")
+    o, Sf = stf(_arr(g["q"]), _arr(g["k"]), _arr(g["v"]), np.asarray(g["S0"], np.float64))
+    assert np.array_equal(np.asarray(o), np.asarray(g["o"], np.float64))
+    assert np.array_equal(np.asarray(Sf), np.asarray(g["S_final"], np.float64))
+
+
+def check_state_closed_form(stf, n=45, d=6, seed=31, tol=1e-12):
+    """Library routine: o = tril(Q K^T) V + Q S0 and S_final = S0 + K^T V."""
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((n, d)).astype(np.float32) for _ in range(3))
+    S0 = rng.standard_normal((d, d))
+    o, Sf = stf(q, k, v, S0)
+    q64, k64, v64 = (x.astype(np.float64) for x in (q, k, v))
+    ref = np.tril(q64 @ k64.T) @ v64 + q64 @ S0
+    assert np.allclose(o, ref, rtol=0, atol=tol * np.abs(ref).max())
+    sref = S0 + k64.T @ v64
+    assert np.allclose(Sf, sref, rtol=0, atol=tol * np.abs(sref).max())
+
+
+def check_state_resume(stf, n=70, d=5, cuts=(1, 16, 33, 69), seed=37, tol=1e-12):
+    """Invariant: a unit run in two pieces, the second continued from the
+    first's final state, equals the run in one piece."""
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((n, d)).astype(np.float32) for _ in range(3))
+    S0 = rng.standard_normal((d, d))
+    o, Sf = stf(q, k, v, S0)
+    for m in cuts:
+        o1, S1 = stf(q[:m], k[:m], v[:m], S0)
+        o2, S2 = stf(q[m:], k[m:], v[m:], S1)
+        oo = np.concatenate([np.asarray(o1), np.asarray(o2)])
+        assert np.allclose(oo, o, rtol=0, atol=tol * np.abs(o).max())
+        assert np.allclose(S2, Sf, rtol=0, atol=tol * np.abs(Sf).max())
+
+
+def check_state_exact(stf, n=9, d=3, seed=41):
+    """Small integers: exact rational o_t = q_t (S0 + sum_{j<=t} k_j^T v_j)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.integers(-3, 4, size=(n, d)).astype(np.float32) for _ in range(3))
+    S0 = rng.integers(-5, 6, size=(d, d)).astype(np.float64)
+    S = [[Fraction(int(S0[a, b])) for b in range(d)] for a in range(d)]
+    exp = []
+    for t in range(n):
+        for a in range(d):
+            for b in range(d):
+                S[a][b] += Fraction(int(k[t, a])) * Fraction(int(v[t, b]))
+        exp.append([float(sum(Fraction(int(q[t, a])) * S[a][b] for a in range(d))) for b in range(d)])
+    o, Sf = stf(q, k, v, S0)
+    assert np.array_equal(np.asarray(o), np.asarray(exp, np.float64))
+    assert np.array_equal(np.asarray(Sf), np.asarray([[float(x) for x in row] for row in S]))

@@ -127,6 +127,45 @@ def test_rel_err_metric(O):
     assert O.rel_err([1.5, -4.0], [1.0, -4.0]) == pytest.approx(0.125)
 
 
+def stf(O):
+    return lambda q, k, v, S0: O.causal_linear_attention_state(q, k, v, S0)
+
+
+def test_state_handoff(O):
+    f = stf(O)
+    pins.check_golden_state(f)
+    pins.check_state_closed_form(f)
+    pins.check_state_resume(f)
+    pins.check_state_exact(f)
+
+
+def test_state_batched_and_varlen(O):
+    """The batched and packed drivers give each unit its own state, and a
+    packed sequence of length 0 ends in its initial state."""
+    rng = np.random.default_rng(43)
+    q, k, v = (rng.standard_normal((2, 3, 19, 4)).astype(np.float32) for _ in range(3))
+    S0 = rng.standard_normal((2, 3, 4, 4))
+    o, Sf = O.causal_linear_attention_state(q, k, v, S0)
+    for b in range(2):
+        for h in range(3):
+            o1, S1 = O.recurrent_final_state(q[b, h], k[b, h], v[b, h], S0[b, h])
+            assert np.array_equal(o[b, h], o1) and np.array_equal(Sf[b, h], S1)
+    lengths = [5, 0, 9]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    qp, kp, vp = (rng.standard_normal((3, T, 4)).astype(np.float32) for _ in range(3))
+    S0p = rng.standard_normal((3, 3, 4, 4))
+    op, Sfp = O.causal_linear_attention_varlen_state(qp, kp, vp, cu, S0p)
+    for s in range(3):
+        for h in range(3):
+            a, e = cu[s], cu[s + 1]
+            o1, S1 = O.recurrent_final_state(qp[h, a:e], kp[h, a:e], vp[h, a:e], S0p[s, h])
+            assert np.array_equal(op[h, a:e], o1) and np.array_equal(Sfp[s, h], S1)
+    assert np.array_equal(Sfp[1], S0p[1])
+    o0, Sf0 = O.causal_linear_attention_varlen_state(qp, kp, vp, cu, None)
+    assert np.array_equal(o0, O.causal_linear_attention_varlen(qp, kp, vp, cu))
+
+
 # ------------------------------------------------- mutants: the pins must bite
 
 def _np_causal(q, k, v, strict=False, transpose_state=False):
@@ -184,6 +223,20 @@ def _varlen_no_reset(q, k, v, cu):
     return o
 
 
+def _np_state(q, k, v, S0, ignore_in_o=False, transpose_s0=False, final_without_s0=False):
+    q = q.astype(np.float64); k = k.astype(np.float64); v = v.astype(np.float64)
+    S0 = np.asarray(S0, np.float64)
+    S0 = S0.T if transpose_s0 else S0
+    n, d = q.shape
+    out = np.zeros((n, d))
+    S = np.zeros((d, d)) if ignore_in_o else S0.copy()
+    for t in range(n):
+        S += np.outer(k[t], v[t])
+        out[t] = q[t] @ S
+    Sf = k.T @ v if final_without_s0 else (S if not ignore_in_o else S0 + S)
+    return out, Sf
+
+
 def _fails(fn, *args):
     try:
         fn(*args)
@@ -217,3 +270,21 @@ def test_mutants_are_caught():
     assert _fails(pins.check_decode_vs_prefill, _dec_update_first, good)
     # packed sequences that leak state across boundaries
     assert _fails(pins.check_varlen_resets, _varlen_no_reset, good)
+    # state handoff: the initial state ignored by o, used transposed, or
+    # missing from the final state
+    stf_good = lambda q, k, v, S0: _np_state(q, k, v, S0)
+    pins.check_golden_state(stf_good)
+    pins.check_state_closed_form(stf_good)
+    pins.check_state_resume(stf_good)
+    pins.check_state_exact(stf_good)
+    no_init = lambda q, k, v, S0: _np_state(q, k, v, S0, ignore_in_o=True)
+    assert _fails(pins.check_golden_state, no_init)
+    assert _fails(pins.check_state_closed_form, no_init)
+    assert _fails(pins.check_state_resume, no_init)
+    s0_t = lambda q, k, v, S0: _np_state(q, k, v, S0, transpose_s0=True)
+    assert _fails(pins.check_golden_state, s0_t)
+    assert _fails(pins.check_state_closed_form, s0_t)
+    assert _fails(pins.check_state_exact, s0_t)
+    no_carry = lambda q, k, v, S0: _np_state(q, k, v, S0, final_without_s0=True)
+    assert _fails(pins.check_golden_state, no_carry)
+    assert _fails(pins.check_state_resume, no_carry)
