@@ -94,6 +94,32 @@ int lightning_attn_fwd(const void *q, const void *k, const void *v, void *o,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * lightning_attn_fwd with a state handoff: each sequence may start from a
+ * given d x d state and its state after its last token may be returned, so
+ * a prefill can hand its state to lightning_attn_decode, or a sequence can
+ * be prefilled in pieces (wiki page "MiniMax-01 Lightning Attention", section
+ * "Lightning Attention 设计": the KV state carries everything the earlier
+ * tokens contribute; Tencent Cloud article, section 4.1).
+ *   s_init:  NULL (every sequence starts from zero, as lightning_attn_fwd) or
+ *            DEVICE fp32 [batch][heads][head_dim][head_dim], state[a][b] with
+ *            a = key dimension, b = value dimension (the decode state layout);
+ *            read only.
+ *   s_final: NULL (not wanted) or DEVICE fp32, same layout: receives
+ *            S_final = s_init + sum over the sequence of k^T v (a sequence of
+ *            length 0 gets its s_init, or zero).
+ * Then o_i = q_i (s_init + sum_{j <= i} k_j^T v_j).  s_final may be the same
+ * buffer as s_init (updated in place); other overlaps between s_final and
+ * any buffer are not allowed.  Both must be 16-byte aligned (else LA_EINVAL).
+ * All other arguments, checks and rules are those of lightning_attn_fwd; when
+ * seq_len == 0 only s_final is written (no workspace is needed).
+ */
+int lightning_attn_fwd_state(const void *q, const void *k, const void *v, void *o,
+                             int batch, int heads, int64_t seq_len, int head_dim, int block_size,
+                             const int32_t *cu_seqlens, int dtype,
+                             const float *s_init, float *s_final,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * lightning_attn_fwd with stage timing: identical work and results, and in
  * addition records caller-created hipEvent_t handles (passed as void*) on
  * `stream` at the stage boundaries, so a caller can time each kernel on the

@@ -61,6 +61,9 @@ def load_library():
     lib.lightning_attn_fwd_chunk_tokens.restype = i64
     lib.lightning_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, i32, vp, sz, vp]
     lib.lightning_attn_fwd.restype = i32
+    lib.lightning_attn_fwd_state.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, i32, vp, vp,
+                                             vp, sz, vp]
+    lib.lightning_attn_fwd_state.restype = i32
     lib.lightning_attn_fwd_traced.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, i32, vp, sz,
                                               vp, ctypes.POINTER(vp), i32]
     lib.lightning_attn_fwd_traced.restype = i32
@@ -98,6 +101,14 @@ def lightning_attn_fwd(q, k, v, o, batch, heads, seq_len, head_dim, block_size, 
     return int(load_library().lightning_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, heads, seq_len, head_dim, block_size,
         _ptr(cu_seqlens), dtype, _ptr(workspace), workspace_bytes, stream))
+
+
+def lightning_attn_fwd_state(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens,
+                             dtype, s_init, s_final, workspace, workspace_bytes, stream) -> int:
+    return int(load_library().lightning_attn_fwd_state(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, heads, seq_len, head_dim, block_size,
+        _ptr(cu_seqlens), dtype, _ptr(s_init), _ptr(s_final), _ptr(workspace), workspace_bytes,
+        stream))
 
 
 def lightning_attn_fwd_traced(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens,
@@ -146,11 +157,16 @@ def workspace_for(q, block_size: int, cu_seqlens=None):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device), nbytes
 
 
-def fwd(q, k, v, block_size: int = 256, cu_seqlens=None, out=None, workspace=None):
+def fwd(q, k, v, block_size: int = 256, cu_seqlens=None, out=None, workspace=None,
+        s_init=None, s_final=None):
     """Causal linear attention forward on the current stream.
 
     Dense: q, k, v [batch, heads, n, d].  Packed: q, k, v [heads, T, d] with
     cu_seqlens an int32 device tensor of nseq+1 offsets.  Returns o (q's dtype).
+    s_init / s_final: optional contiguous fp32 device tensors [nseq, heads, d, d]
+    (nseq = batch for dense input): the state each sequence starts from, and
+    the tensor that receives each sequence's state after its last token (it
+    may be s_init itself).
     """
     import torch
     for t in (q, k, v):
@@ -172,8 +188,17 @@ def fwd(q, k, v, block_size: int = 256, cu_seqlens=None, out=None, workspace=Non
         heads, n, d = q.shape
         batch = cu_seqlens.numel() - 1
         cu = cu_seqlens
-    st = lightning_attn_fwd(q, k, v, o, batch, heads, n, d, block_size, cu, _dtype_code(q),
-                            workspace if nbytes else None, nbytes, _stream_handle(q.device))
+    for x in (s_init, s_final):
+        if x is not None and (x.dtype != torch.float32 or not x.is_contiguous() or not x.is_cuda
+                              or tuple(x.shape) != (batch, heads, d, d)):
+            raise ValueError("s_init / s_final must be contiguous fp32 device tensors [nseq, heads, d, d]")
+    if s_init is None and s_final is None:
+        st = lightning_attn_fwd(q, k, v, o, batch, heads, n, d, block_size, cu, _dtype_code(q),
+                                workspace if nbytes else None, nbytes, _stream_handle(q.device))
+    else:
+        st = lightning_attn_fwd_state(q, k, v, o, batch, heads, n, d, block_size, cu, _dtype_code(q),
+                                      s_init, s_final, workspace if nbytes else None, nbytes,
+                                      _stream_handle(q.device))
     if st != LA_OK:
         raise LightningAttnError(st, "lightning_attn_fwd")
     return o

@@ -121,16 +121,22 @@ int64_t lightning_attn_fwd_chunk_tokens(int batch, int heads, int64_t seq_len, i
 
 static int fwd_common(const void *q, const void *k, const void *v, void *o, int batch, int heads,
                       int64_t seq_len, int head_dim, int block_size, const int32_t *cu_seqlens,
-                      int dtype, void *workspace, size_t workspace_bytes, void *stream,
-                      void *const *events) {
+                      int dtype, const float *s_init, float *s_final, void *workspace,
+                      size_t workspace_bytes, void *stream, void *const *events) {
     int st = la::check_fwd_shape(batch, heads, seq_len, head_dim, block_size, dtype);
     if (st != LA_OK) return st;
-    if (seq_len == 0) return LA_OK;
+    if (((uintptr_t)s_init & 15) != 0 || ((uintptr_t)s_final & 15) != 0) return LA_EINVAL;
+    if (seq_len == 0) {
+        // no tokens: only the final states (each equal to its initial state)
+        if (!s_final) return LA_OK;
+        return la::launch_state_empty(s_init, s_final, batch, heads, head_dim, stream) == 0 ? LA_OK : LA_EHIP;
+    }
     if (!q || !k || !v || !o) return LA_EINVAL;
     la::FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o;
     a.nseq = batch; a.heads = heads; a.head_dim = head_dim; a.block_size = block_size;
     a.dtype = dtype; a.seq_len = seq_len; a.cu_seqlens = cu_seqlens;
+    a.s_init = s_init; a.s_final = s_final;
     la::make_fwd_plan(batch, heads, seq_len, head_dim, block_size, cu_seqlens != nullptr, &a.plan);
     if (!workspace || workspace_bytes < a.plan.bytes) return LA_EWORKSPACE;
     if (((uintptr_t)workspace & 255) != 0) return LA_EINVAL;
@@ -142,7 +148,16 @@ int lightning_attn_fwd(const void *q, const void *k, const void *v, void *o, int
                        int64_t seq_len, int head_dim, int block_size, const int32_t *cu_seqlens,
                        int dtype, void *workspace, size_t workspace_bytes, void *stream) {
     return fwd_common(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens, dtype,
-                      workspace, workspace_bytes, stream, nullptr);
+                      nullptr, nullptr, workspace, workspace_bytes, stream, nullptr);
+}
+
+int lightning_attn_fwd_state(const void *q, const void *k, const void *v, void *o, int batch,
+                             int heads, int64_t seq_len, int head_dim, int block_size,
+                             const int32_t *cu_seqlens, int dtype, const float *s_init,
+                             float *s_final, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+    return fwd_common(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens, dtype,
+                      s_init, s_final, workspace, workspace_bytes, stream, nullptr);
 }
 
 int lightning_attn_fwd_traced(const void *q, const void *k, const void *v, void *o, int batch,
@@ -154,7 +169,7 @@ int lightning_attn_fwd_traced(const void *q, const void *k, const void *v, void 
     for (int i = 0; i < nevents; ++i)
         if (!events[i]) return LA_EINVAL;
     return fwd_common(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens, dtype,
-                      workspace, workspace_bytes, stream, events);
+                      nullptr, nullptr, workspace, workspace_bytes, stream, events);
 }
 
 int lightning_attn_decode(const void *q, const void *k, const void *v, float *state, void *o, int batch,

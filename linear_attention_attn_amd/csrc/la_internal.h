@@ -40,6 +40,8 @@ struct FwdArgs {
     int nseq, heads, head_dim, block_size, dtype;
     int64_t seq_len;          // dense: tokens per sequence; packed: total tokens
     const int32_t *cu_seqlens;  // device, or nullptr for dense input
+    const float *s_init;      // device [nseq][heads][d][d] or nullptr (zero)
+    float *s_final;           // device [nseq][heads][d][d] or nullptr (not wanted)
     char *workspace;
     FwdPlan plan;
 };
@@ -48,6 +50,11 @@ struct FwdArgs {
 // non-null it holds 5 hipEvent_t handles recorded at the stage boundaries.
 // Returns 0 or a HIP error code.
 int launch_fwd(const FwdArgs &a, void *stream, void *const *events);
+
+// Queue the kernel that sets the final state of every sequence of length 0
+// (all of them when there are no tokens at all) to its initial state.
+int launch_state_empty(const float *s_init, float *s_final, int nseq, int heads, int head_dim,
+                       void *stream);
 
 // Queue one decode step.  Returns 0 or a HIP error code.
 int launch_decode(const void *q, const void *k, const void *v, float *state, void *o,

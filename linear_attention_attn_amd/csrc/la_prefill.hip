@@ -39,6 +39,13 @@ struct KParams {
     int64_t chunk;          // tokens per chunk
     int64_t nchunk_ub, ntile_ub;
     int nseq, heads, group;
+    // state handoff: initial states [nseq][heads][D][D] (or nullptr = zero)
+    // and final states of the same layout (or nullptr = not wanted).
+    // init_mode 0: no initial state; 1: the scan adds it to every chunk's
+    // prefix in `states`; 2: one chunk per sequence, read directly.
+    const float *s_init;
+    float *s_final;
+    int init_mode;
 };
 
 // ------------------------------------------------------------------ units
@@ -70,6 +77,37 @@ __device__ __forceinline__ int find_seg(const int32_t *off, int n, int64_t x) {
         if ((int64_t)off[mid] <= x) lo = mid; else hi = mid;
     }
     return lo;
+}
+
+// Source of the state at the start of chunk gch (chunk-local index cl) of
+// sequence s, head h, or nullptr for zero: the scanned prefix in `states`
+// (which includes a carried-in initial state when one was given), or with
+// one chunk per sequence the initial state itself.
+template <int D>
+__device__ __forceinline__ const float *chunk_start_state(const KParams &p, int s, int h, int64_t gch,
+                                                          int64_t cl) {
+    if (p.init_mode == 2) return p.s_init + ((int64_t)s * p.heads + h) * (D * D);
+    if (p.init_mode == 0 && cl == 0) return nullptr;
+    return p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
+}
+
+// Final state of (s, h) when the caller asked for it and chunk gch is the
+// sequence's last: the workgroup of that chunk writes it; else nullptr.
+template <int D>
+__device__ __forceinline__ float *final_state_dst(const KParams &p, int s, int h, int64_t gch) {
+    if (p.s_final == nullptr || gch + 1 != p.chunk_off[s + 1]) return nullptr;
+    return p.s_final + ((int64_t)s * p.heads + h) * (D * D);
+}
+
+// Final state of sequences with no tokens: the initial state (or zero).
+template <int D>
+__global__ __launch_bounds__(256) void k_state_empty(KParams p) {
+    const int s = blockIdx.x, h = blockIdx.y;
+    const int64_t L = p.cu ? (int64_t)p.cu[s + 1] - p.cu[s] : p.seq_len;
+    if (L != 0) return;
+    float *dst = p.s_final + ((int64_t)s * p.heads + h) * (D * D);
+    const float *src = p.s_init ? p.s_init + ((int64_t)s * p.heads + h) * (D * D) : nullptr;
+    for (int e = threadIdx.x; e < D * D; e += 256) dst[e] = src ? src[e] : 0.f;
 }
 
 // -------------------------------------------------------------- k_prep
@@ -353,11 +391,24 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_apply(KParams p, int use_
     const int e = blockIdx.y * kScanThreads + threadIdx.x;
     float *st = p.states + (int64_t)h * p.nchunk_ub * (D * D) + e;
     float run = use_tiles ? p.tilesum[((int64_t)h * p.ntile_ub + tile) * (D * D) + e] : 0.f;
+    if (p.s_init) run += p.s_init[((int64_t)s * p.heads + h) * (D * D) + e];   // carried-in state
     for (int64_t c = c0; c < c1; ++c) {
         const float x = st[c * (D * D)];
         st[c * (D * D)] = run;
         run += x;
     }
+}
+
+// fp32 state tiles of a wave (its SA x SB grid of 16 x 16 tiles at a0, b0;
+// lane (c, g) holds rows 4g .. 4g+3, column c of each) to global memory.
+template <int D, int SA, int SB>
+__device__ __forceinline__ void store_state(float *dst, const f32x4_t (&S)[SA][SB], int a0, int b0, int c, int g) {
+#pragma unroll
+    for (int ia = 0; ia < SA; ++ia)
+#pragma unroll
+        for (int ib = 0; ib < SB; ++ib)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c] = S[ia][ib][r];
 }
 
 // ----------------------------------------------------------- k_fused
@@ -388,16 +439,16 @@ __global__ __launch_bounds__(512, 1) void k_fused(KParams p) {
 
     // ---- state at the chunk start (exclusive prefix from the scan)
     f32x4_t S[C::SA][C::SB];
+    float *const fdst = final_state_dst<D>(p, s, h, gch);
     {
-        const float *src = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
-        const bool first = cl == 0;
+        const float *src = chunk_start_state<D>(p, s, h, gch, cl);
 #pragma unroll
         for (int ia = 0; ia < C::SA; ++ia)
 #pragma unroll
             for (int ib = 0; ib < C::SB; ++ib)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    S[ia][ib][r] = first ? 0.f : src[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c];
+                    S[ia][ib][r] = src ? src[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c] : 0.f;
 #pragma unroll
         for (int ia = 0; ia < C::SA; ++ia)
 #pragma unroll
@@ -518,7 +569,7 @@ __global__ __launch_bounds__(512, 1) void k_fused(KParams p) {
             // Q of this block is dead after the last tile's scores: fetch the next block's
             if (last && more) load_q(tb + BLK);
             // ---- state for the next block of this chunk
-            if (more) state_update<T, D, BLK, C::SA, C::SB>(S, kt, vt, a0, b0);
+            if (more || fdst) state_update<T, D, BLK, C::SA, C::SB>(S, kt, vt, a0, b0);
 
             if (nxt) {
                 if (NBUF == 1) __syncthreads();
@@ -548,6 +599,7 @@ __global__ __launch_bounds__(512, 1) void k_fused(KParams p) {
             __syncthreads();
         }
     }
+    if (fdst) store_state<D, C::SA, C::SB>(fdst, S, a0, b0, c, g);
 }
 
 // ================================================================ bf16 path
@@ -951,16 +1003,16 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     load_q(Q, 0, 0, C::KC);
     issue(0, stages[0]);
     if constexpr (LA >= 3) issue(1, stages[1]);
+    float *const fdst = final_state_dst<D>(p, s, h, gch);
     {
-        const float *src = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
-        const bool first = cl == 0;
+        const float *src = chunk_start_state<D>(p, s, h, gch, cl);
 #pragma unroll
         for (int ia = 0; ia < C::SA; ++ia)
 #pragma unroll
             for (int ib = 0; ib < C::SB; ++ib)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    S[ia][ib][r] = first ? 0.f : src[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c];
+                    S[ia][ib][r] = src ? src[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c] : 0.f;
         write_state(S);
     }
     wait_vm_lgkm0<0>();
@@ -1113,8 +1165,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
 
         if constexpr (last) {
             if constexpr (TPB == 1) load_q(Q, tb + BLK, 0, C::KC);   // this block's Q is dead after its scores
+            if (more || fdst) state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
             if (more) {
-                state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
                 if constexpr (first) {               // one-tile blocks: the state copy was read in this tile
                     wait_vm_lgkm0<63>();
                     wg_barrier();
@@ -1135,7 +1187,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
             }
             if constexpr (LA > 1) issue(t + LA, stages[(J + LA) % NST]);
         } else {
-            if (more) state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
+            if (more || fdst) state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
             // DMA(t+1) has landed; younger are DMA(t+2 .. t+LA) and the Q
             // loads of the LA-1 tiles up to this one
             wait_vm_lgkm0<(LA - 1) * IPW + (LA >= 2 ? QS::n(jt) : 0) + (LA >= 3 ? QS::n(jt - 1) : 0)>();
@@ -1152,6 +1204,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         tile(integral_constant<int, 3>{}, sb);
     }
     wait_vm_lgkm0<0>();                              // DMA past the chunk end and the stores are done
+    if (fdst) {
+        const int lf = lane_id_fresh();
+        store_state<D, C::SA, C::SB>(fdst, S, a0, b0, lf & 15, lf >> 4);
+    }
 }
 
 // -------------------------------------------------------------- host side
@@ -1167,6 +1223,7 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
     const dim3 gchunks((unsigned)plan.nchunk_ub, (unsigned)kp.heads);
     mark(0);
     hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, st, kp);
+    if (kp.s_final) hipLaunchKernelGGL(k_state_empty<D>, dim3(kp.nseq, kp.heads), dim3(256), 0, st, kp);
     mark(1);
     // Every chunk but the first of its sequence needs the exclusive prefix of
     // the chunk summaries before it; with one chunk per sequence there is none.
@@ -1208,6 +1265,21 @@ static hipError_t launch_blk(const KParams &kp, const FwdPlan &plan, int blk, hi
     }
 }
 
+int launch_state_empty(const float *s_init, float *s_final, int nseq, int heads, int head_dim,
+                       void *stream) {
+    KParams kp{};
+    kp.seq_len = 0;
+    kp.cu = nullptr;
+    kp.nseq = nseq;
+    kp.heads = heads;
+    kp.s_init = s_init;
+    kp.s_final = s_final;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (head_dim == 64) hipLaunchKernelGGL(k_state_empty<64>, dim3(nseq, heads), dim3(256), 0, st, kp);
+    else hipLaunchKernelGGL(k_state_empty<128>, dim3(nseq, heads), dim3(256), 0, st, kp);
+    return (int)hipGetLastError();
+}
+
 int launch_fwd(const FwdArgs &a, void *stream, void *const *events) {
     KParams kp;
     kp.q = a.q; kp.k = a.k; kp.v = a.v; kp.o = a.o;
@@ -1223,6 +1295,9 @@ int launch_fwd(const FwdArgs &a, void *stream, void *const *events) {
     kp.nseq = a.nseq;
     kp.heads = a.heads;
     kp.group = a.plan.scan_group;
+    kp.s_init = a.s_init;
+    kp.s_final = a.s_final;
+    kp.init_mode = a.s_init == nullptr ? 0 : (a.plan.single_chunk ? 2 : 1);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (a.dtype == 0) {
