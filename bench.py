@@ -147,6 +147,56 @@ def bench_prefill(w, steps, warmup, dev, traced=True):
     return (t1 - t0) * 1000.0 / steps, stage, chunk, nbytes
 
 
+def bench_prefill_state(w, steps, warmup, dev):
+    """The prefill workload through lightning_attn_fwd_state, each sequence
+    starting from a state and returning its final state (in place)."""
+    import torch
+    import linear_attention_attn_amd as la
+    import synth
+
+    q, k, v = synth.prefill_inputs(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype, w.cid, dev)
+    o = torch.empty_like(q)
+    S = synth.decode_state(w.batch, w.heads, w.head_dim, w.cid, dev)
+    code = la.LA_DTYPE_BF16 if w.dtype == "bf16" else la.LA_DTYPE_F32
+    nbytes = la.lightning_attn_fwd_workspace_size(w.batch, w.heads, w.seq_len, w.head_dim,
+                                                  w.block_size, 0, code)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def with_state():
+        st = la.lightning_attn_fwd_state(q, k, v, o, w.batch, w.heads, w.seq_len, w.head_dim,
+                                         w.block_size, None, code, S, S, ws, nbytes, stream)
+        if st != la.LA_OK:
+            raise la.LightningAttnError(st, "lightning_attn_fwd_state")
+
+    def plain():
+        st = la.lightning_attn_fwd(q, k, v, o, w.batch, w.heads, w.seq_len, w.head_dim,
+                                   w.block_size, None, code, ws, nbytes, stream)
+        if st != la.LA_OK:
+            raise la.LightningAttnError(st, "lightning_attn_fwd")
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    # alternate the two so that both see the same clocks
+    ms_plain, ms_state = [], []
+    for _ in range(2):
+        ms_plain.append(timed(plain))
+        ms_state.append(timed(with_state))
+    del q, k, v, o, S, ws
+    torch.cuda.empty_cache()
+    return min(ms_state), min(ms_plain)
+
+
 def bench_decode(w, reps, dev):
     import torch
     import linear_attention_attn_amd as la
@@ -334,6 +384,15 @@ def main():
         out["decode"] = {"workload": wd.note, "ms_per_step": dms, "gbs": dgbs,
                          "hbm_frac": dgbs / PEAK_HBM_GBS, "head_steps_per_s": dtok}
         log(json.dumps(out["decode"]))
+        sms, pms = bench_prefill_state(w, args.steps, args.warmup, dev)
+        out["state_handoff"] = {
+            "workload": f"{w.name} through lightning_attn_fwd_state: every sequence starts from a "
+                        "state and returns its final state (in place)",
+            "ms_per_step": sms, "tokens_per_s": tokens / (sms * 1e-3),
+            "ms_per_step_plain_same_timing": pms,
+            "state_bytes": w.batch * w.heads * 2 * 4 * d * d,
+            "overhead_vs_plain": sms / pms - 1.0}
+        log(json.dumps(out["state_handoff"]))
         wl = synth.WORKLOADS["long_1m"]
         log(f"prefill {wl.name}: {wl.note}")
         lms, lstage, lchunk, _ = bench_prefill(wl, 5, 3, dev)
