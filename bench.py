@@ -234,6 +234,59 @@ def bench_decode(w, reps, dev):
     return best, bytes_step / (best * 1e-3) / 1e9, units / (best * 1e-3)
 
 
+def bench_decode_indexed(w, reps, dev, pad_rows=64):
+    """The decode workload over an indexed state table: a pool of twice as
+    many states, rows mapped to shuffled slots, and the same with the batch
+    padded by pad_rows padding rows (slot -1)."""
+    import numpy as np
+    import torch
+    import linear_attention_attn_amd as la
+    import synth
+
+    pool = synth.decode_state(2 * w.batch, w.heads, w.head_dim, w.cid, dev)
+    rng = np.random.default_rng(w.cid)
+    live = rng.permutation(2 * w.batch)[:w.batch].astype(np.int32)
+    padded = np.full(w.batch + pad_rows, -1, np.int32)
+    where = np.sort(rng.permutation(w.batch + pad_rows)[:w.batch])
+    padded[where] = live
+    code = la.LA_DTYPE_BF16 if w.dtype == "bf16" else la.LA_DTYPE_F32
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    out = {}
+    for name, sl in (("shuffled", live), ("padded", padded)):
+        rows = len(sl)
+        slots = torch.tensor(sl, device=dev)
+        ins = [tuple(torch.nn.functional.pad(x, (0, 0, 0, 0, 0, rows - w.batch)).contiguous() for x in
+                     synth.decode_step_inputs(w.batch, w.heads, w.head_dim, w.dtype, w.cid, t, dev))
+               for t in range(w.steps)]
+        o = torch.empty_like(ins[0][0])
+
+        def run_all():
+            for q, k, v in ins:
+                st = la.lightning_attn_decode_indexed(q, k, v, pool, 2 * w.batch, slots, o, rows,
+                                                      w.heads, w.head_dim, code, stream)
+                if st != la.LA_OK:
+                    raise la.LightningAttnError(st, "lightning_attn_decode_indexed")
+
+        run_all()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = None
+        for _ in range(reps):
+            a.record()
+            run_all()
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / w.steps
+            best = ms if best is None else min(best, ms)
+        live_bytes = w.batch * w.heads * (8 * w.head_dim ** 2 + 8 * w.head_dim)
+        out[name] = {"rows": rows, "live_rows": w.batch, "ms_per_step": best,
+                     "gbs_live": live_bytes / (best * 1e-3) / 1e9}
+        del ins, o
+    del pool
+    torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration(dev, nbytes=1 << 30, reps=5):
     """A plain device-to-device copy of known size (reads nbytes, writes nbytes)."""
     import torch
@@ -384,6 +437,10 @@ def main():
         out["decode"] = {"workload": wd.note, "ms_per_step": dms, "gbs": dgbs,
                          "hbm_frac": dgbs / PEAK_HBM_GBS, "head_steps_per_s": dtok}
         log(json.dumps(out["decode"]))
+        out["decode_indexed"] = bench_decode_indexed(wd, 5, dev)
+        out["decode_indexed"]["workload"] = (f"{wd.note}; states in a pool of {2 * wd.batch} x {wd.heads}, "
+                                             "rows on shuffled slots; 'padded' adds 64 padding rows")
+        log(json.dumps(out["decode_indexed"]))
         sms, pms = bench_prefill_state(w, args.steps, args.warmup, dev)
         out["state_handoff"] = {
             "workload": f"{w.name} through lightning_attn_fwd_state: every sequence starts from a "

@@ -153,6 +153,26 @@ int lightning_attn_fwd_traced(const void *q, const void *k, const void *v, void 
 int lightning_attn_decode(const void *q, const void *k, const void *v, float *state, void *o,
                           int batch, int heads, int head_dim, int dtype, void *stream);
 
+/*
+ * One decode step over an indexed state table, for serving batches whose
+ * sequences come and go while their states stay in a pool (the wiki page's
+ * section "计算优化" lists separate prefill and decoding execution and
+ * multi-level padding among the inference optimisations): row b of the
+ * batch uses pool entry slots[b].
+ *   state_pool: fp32 [nslots][heads][head_dim][head_dim] (decode layout);
+ *   slots:      DEVICE int32 [batch]; a slot < 0 or >= nslots marks a padding
+ *               row: its o is written as zero and no state is touched, so a
+ *               caller can pad a batch up to one of a few fixed sizes;
+ *   q, k, v, o: [batch][heads][head_dim] in `dtype`.
+ * For every non-padding row: o = q . S_old, S_new = S_old + k^T v, with S the
+ * pool entry, updated in place.  Two non-padding rows must not name the same
+ * slot (precondition, not checked).  state_pool may be NULL only when
+ * nslots == 0 (then every row is padding).  Checks happen on the host first.
+ */
+int lightning_attn_decode_indexed(const void *q, const void *k, const void *v, float *state_pool,
+                                  int nslots, const int32_t *slots, void *o, int batch, int heads,
+                                  int head_dim, int dtype, void *stream);
+
 /* Static, human-readable text for a status code. */
 const char *lightning_attn_strerror(int status);
 

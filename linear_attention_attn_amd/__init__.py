@@ -69,6 +69,8 @@ def load_library():
     lib.lightning_attn_fwd_traced.restype = i32
     lib.lightning_attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]
     lib.lightning_attn_decode.restype = i32
+    lib.lightning_attn_decode_indexed.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, vp]
+    lib.lightning_attn_decode_indexed.restype = i32
     lib.lightning_attn_strerror.argtypes = [i32]
     lib.lightning_attn_strerror.restype = ctypes.c_char_p
     _LIB = lib
@@ -122,6 +124,13 @@ def lightning_attn_fwd_traced(q, k, v, o, batch, heads, seq_len, head_dim, block
 def lightning_attn_decode(q, k, v, state, o, batch, heads, head_dim, dtype, stream) -> int:
     return int(load_library().lightning_attn_decode(
         _ptr(q), _ptr(k), _ptr(v), _ptr(state), _ptr(o), batch, heads, head_dim, dtype, stream))
+
+
+def lightning_attn_decode_indexed(q, k, v, state_pool, nslots, slots, o, batch, heads, head_dim,
+                                  dtype, stream) -> int:
+    return int(load_library().lightning_attn_decode_indexed(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(state_pool), nslots, _ptr(slots), _ptr(o), batch, heads,
+        head_dim, dtype, stream))
 
 
 def lightning_attn_strerror(status: int) -> str:
@@ -220,4 +229,29 @@ def decode(q, k, v, state, out=None):
                                _stream_handle(q.device))
     if st != LA_OK:
         raise LightningAttnError(st, "lightning_attn_decode")
+    return o
+
+
+def decode_indexed(q, k, v, state_pool, slots, out=None):
+    """One decode step over a pool of states: row b uses state_pool[slots[b]]
+    (in place); rows with a slot outside [0, len(state_pool)) are padding
+    (o row zero, nothing else touched).
+
+    q, k, v: [batch, heads, d]; state_pool: fp32 [nslots, heads, d, d];
+    slots: int32 device tensor [batch].
+    """
+    import torch
+    if state_pool.dtype != torch.float32 or not state_pool.is_contiguous():
+        raise ValueError("state_pool must be a contiguous fp32 tensor")
+    batch, heads, d = q.shape
+    nslots = state_pool.shape[0]
+    if tuple(state_pool.shape[1:]) != (heads, d, d):
+        raise ValueError("state_pool shape must be [nslots, heads, d, d]")
+    if slots.dtype != torch.int32 or not slots.is_cuda or slots.numel() != batch:
+        raise ValueError("slots must be an int32 device tensor of batch entries")
+    o = torch.empty_like(q) if out is None else out
+    st = lightning_attn_decode_indexed(q, k, v, state_pool, nslots, slots, o, batch, heads, d,
+                                       _dtype_code(q), _stream_handle(q.device))
+    if st != LA_OK:
+        raise LightningAttnError(st, "lightning_attn_decode_indexed")
     return o

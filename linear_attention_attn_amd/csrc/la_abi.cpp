@@ -182,6 +182,19 @@ int lightning_attn_decode(const void *q, const void *k, const void *v, float *st
     return la::launch_decode(q, k, v, state, o, batch, heads, head_dim, dtype, stream) == 0 ? LA_OK : LA_EHIP;
 }
 
+int lightning_attn_decode_indexed(const void *q, const void *k, const void *v, float *state_pool,
+                                  int nslots, const int32_t *slots, void *o, int batch, int heads,
+                                  int head_dim, int dtype, void *stream) {
+    if (!(dtype == LA_DTYPE_BF16 || dtype == LA_DTYPE_F32)) return LA_EUNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return LA_EUNSUPPORTED;
+    if (batch < 1 || heads < 1 || nslots < 0) return LA_EINVAL;
+    if ((int64_t)batch * heads > (int64_t)INT32_MAX || (int64_t)nslots * heads > (int64_t)INT32_MAX)
+        return LA_EUNSUPPORTED;
+    if (!q || !k || !v || !slots || !o || (nslots > 0 && !state_pool)) return LA_EINVAL;
+    return la::launch_decode(q, k, v, state_pool, o, batch, heads, head_dim, dtype, stream, slots,
+                             nslots) == 0 ? LA_OK : LA_EHIP;
+}
+
 const char *lightning_attn_strerror(int status) {
     switch (status) {
         case LA_OK: return "success";

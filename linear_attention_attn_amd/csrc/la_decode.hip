@@ -28,20 +28,39 @@ template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t x) {
 __device__ __forceinline__ void from_f32(float x, float *p) { *p = x; }
 __device__ __forceinline__ void from_f32(float x, bf16_t *p) { p->bits = (uint16_t)bf16_bits_rne(x); }
 
+// With `slots` (an indexed state table, for batches that come and go while
+// their states stay in a pool): row b's state is pool entry slots[b]; rows
+// whose slot is negative or not below `nslots` are padding: their o is
+// zero and no state is touched (so a batch can be padded to a fixed size).
 template <typename T, int D>
 __global__ __launch_bounds__(kDecThreads) void k_decode(const T *__restrict__ q, const T *__restrict__ k,
                                                       const T *__restrict__ v, float *__restrict__ state,
-                                                      T *__restrict__ o) {
+                                                      T *__restrict__ o, const int32_t *__restrict__ slots,
+                                                      int heads, int nslots) {
     constexpr int CT = D / 4;                 // threads across one row (4 columns each)
     constexpr int RG = kDecThreads / CT;      // row groups
     constexpr int RPT = D / RG;               // rows per thread
     __shared__ float sq[D], sk[D];
     __shared__ f32x4_t red[RG][CT];
 
-    const int64_t unit = blockIdx.x;
+    // Workgroups are dealt to the 8 XCDs round-robin; give each XCD a
+    // contiguous range of units (measured ~1.5% faster than unit = blockIdx.x
+    // on MI355X; pseudo-random orders were slower).
+    const int64_t nb = gridDim.x;
+    const int64_t unit = (nb % 8 == 0) ? (int64_t)(blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8 : blockIdx.x;
     const int t = threadIdx.x;
     const T *qu = q + unit * D, *ku = k + unit * D, *vu = v + unit * D;
-    float *S = state + unit * (int64_t)D * D;
+    int64_t su = unit;                        // state entry of this (row, head)
+    if (slots != nullptr) {
+        const int64_t b = unit / heads, h = unit - b * heads;
+        const int slot = slots[b];
+        if (slot < 0 || slot >= nslots) {     // padding row
+            if (t < D) from_f32(0.f, o + unit * D + t);
+            return;
+        }
+        su = (int64_t)slot * heads + h;
+    }
+    float *S = state + su * (int64_t)D * D;
     if (t < D) {
         sq[t] = to_f32(qu[t]);
         sk[t] = to_f32(ku[t]);
@@ -80,7 +99,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const T *__restrict__ q,
 }
 
 int launch_decode(const void *q, const void *k, const void *v, float *state, void *o, int batch,
-                  int heads, int head_dim, int dtype, void *stream) {
+                  int heads, int head_dim, int dtype, void *stream, const int32_t *slots, int nslots) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)((int64_t)batch * heads));
     if (dtype == 0) {
@@ -88,15 +107,15 @@ int launch_decode(const void *q, const void *k, const void *v, float *state, voi
         auto *kk = reinterpret_cast<const bf16_t *>(k);
         auto *vv = reinterpret_cast<const bf16_t *>(v);
         auto *oo = reinterpret_cast<bf16_t *>(o);
-        if (head_dim == 64) hipLaunchKernelGGL((k_decode<bf16_t, 64>), grid, dim3(kDecThreads), 0, st, qq, kk, vv, state, oo);
-        else hipLaunchKernelGGL((k_decode<bf16_t, 128>), grid, dim3(kDecThreads), 0, st, qq, kk, vv, state, oo);
+        if (head_dim == 64) hipLaunchKernelGGL((k_decode<bf16_t, 64>), grid, dim3(kDecThreads), 0, st, qq, kk, vv, state, oo, slots, heads, nslots);
+        else hipLaunchKernelGGL((k_decode<bf16_t, 128>), grid, dim3(kDecThreads), 0, st, qq, kk, vv, state, oo, slots, heads, nslots);
     } else {
         auto *qq = reinterpret_cast<const float *>(q);
         auto *kk = reinterpret_cast<const float *>(k);
         auto *vv = reinterpret_cast<const float *>(v);
         auto *oo = reinterpret_cast<float *>(o);
-        if (head_dim == 64) hipLaunchKernelGGL((k_decode<float, 64>), grid, dim3(kDecThreads), 0, st, qq, kk, vv, state, oo);
-        else hipLaunchKernelGGL((k_decode<float, 128>), grid, dim3(kDecThreads), 0, st, qq, kk, vv, state, oo);
+        if (head_dim == 64) hipLaunchKernelGGL((k_decode<float, 64>), grid, dim3(kDecThreads), 0, st, qq, kk, vv, state, oo, slots, heads, nslots);
+        else hipLaunchKernelGGL((k_decode<float, 128>), grid, dim3(kDecThreads), 0, st, qq, kk, vv, state, oo, slots, heads, nslots);
     }
     return (int)hipGetLastError();
 }

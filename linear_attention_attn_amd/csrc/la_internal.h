@@ -56,8 +56,11 @@ int launch_fwd(const FwdArgs &a, void *stream, void *const *events);
 int launch_state_empty(const float *s_init, float *s_final, int nseq, int heads, int head_dim,
                        void *stream);
 
-// Queue one decode step.  Returns 0 or a HIP error code.
+// Queue one decode step.  With `slots` non-null, row b's state is entry
+// slots[b] of a pool of `nslots` (out-of-range slots are padding rows).
+// Returns 0 or a HIP error code.
 int launch_decode(const void *q, const void *k, const void *v, float *state, void *o,
-                  int batch, int heads, int head_dim, int dtype, void *stream);
+                  int batch, int heads, int head_dim, int dtype, void *stream,
+                  const int32_t *slots = nullptr, int nslots = 0);
 
 }  // namespace la
