@@ -7,7 +7,9 @@ of ``bench.py`` use it.  It shares no code with the HIP path.
 The arithmetic lives in ``la_oracle.c`` (IEEE double, plain loops, built with
 ``-O2 -ffp-contract=off`` and no fast-math).  This module builds that file,
 binds it with ctypes and adds two tiny-input brute forces (numpy matrix form
-and exact rational arithmetic) that are written independently of the C code.
+and exact rational arithmetic) that are written independently of the C code,
+plus the rotary position embedding on half the head dims (numpy float64) and
+causal linear attention over rotated q and k in its closed masked form.
 
 The operation (wiki page "MiniMax-01 Lightning Attention", section
 "Lightning Attention 设计"; Tencent Cloud article, section 4.1):
@@ -218,6 +220,105 @@ def decode(q, k, v, S0, nthreads: int = 0):
     lib.lao_decode_units(_p(q, ctypes.c_float), _p(k, ctypes.c_float), _p(v, ctypes.c_float),
                          _p(S, ctypes.c_double), _p(o, ctypes.c_double), steps, units, d,
                          int(nthreads))
+    return o, S
+
+
+# ---- rotary position embedding on half the head dims ------------------------
+#
+# Wiki page "MiniMax-01 Lightning Attention", section "模型架构": RoPE is
+# applied to half of the attention head dimensions with base frequency
+# 10,000 (raised to 10M for the long-context stage).  The page leaves the
+# rest open; the readings taken here: the rotated dims are the first
+# rope_dims = d/2 of q and k (v is not rotated); dim i < rope_dims/2 pairs with
+# dim i + rope_dims/2; the pair at token position p turns by the angle
+# p * base^(-2i / rope_dims); positions count from 0 at each sequence's first
+# token, plus an optional per-sequence offset (a sequence continued from a
+# carried-in state continues its positions).
+
+def rope(x, positions, rope_dims: int, base: float) -> np.ndarray:
+    """x [..., n, d] rotated at integer positions [..., n] (float64)."""
+    x = np.asarray(x, np.float64)
+    r = int(rope_dims)
+    assert r % 2 == 0 and 0 < r <= x.shape[-1]
+    h = r // 2
+    theta = float(base) ** (-2.0 * np.arange(h, dtype=np.float64) / r)
+    ang = np.asarray(positions, np.float64)[..., None] * theta
+    c, s = np.cos(ang), np.sin(ang)
+    out = x.copy()
+    a, b = x[..., :h], x[..., h:r]
+    out[..., :h] = a * c - b * s
+    out[..., h:r] = a * s + b * c
+    return out
+
+
+def masked_state_form(q, k, v, S0=None):
+    """(o, S_final) for one [n, d] unit in float64 by the closed form
+    o = tril(Q K^T) V + Q S0, S_final = S0 + K^T V (inputs taken as given,
+    no rounding).  Quadratic in n: for the moderate sizes of the tests."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    d = q.shape[-1]
+    S0 = np.zeros((d, d)) if S0 is None else np.asarray(S0, np.float64)
+    return np.tril(q @ k.T) @ v + q @ S0, S0 + k.T @ v
+
+
+def causal_linear_attention_rope(q, k, v, rope_dims: int, base: float, pos_offset=None,
+                                 S0=None):
+    """Dense [B, H, n, d]: q and k rotated at positions pos_offset[b] + t, then
+    causal linear attention from S0 [B, H, d, d] (None = zero).  Returns
+    (o, S_final) in float64."""
+    q = np.asarray(q, np.float64)
+    B, H, n, d = q.shape
+    off = np.zeros(B, np.int64) if pos_offset is None else np.asarray(pos_offset, np.int64)
+    o = np.zeros(q.shape)
+    Sf = np.zeros((B, H, d, d))
+    for b in range(B):
+        pos = off[b] + np.arange(n)
+        for h in range(H):
+            qr = rope(q[b, h], pos, rope_dims, base)
+            kr = rope(k[b, h], pos, rope_dims, base)
+            o[b, h], Sf[b, h] = masked_state_form(qr, kr, v[b, h], None if S0 is None else S0[b, h])
+    return o, Sf
+
+
+def causal_linear_attention_rope_varlen(q, k, v, cu_seqlens, rope_dims: int, base: float,
+                                        pos_offset=None, S0=None):
+    """Packed [H, T, d] (sequence s is tokens [cu[s], cu[s+1])): as
+    causal_linear_attention_rope per sequence; S0 / S_final [nseq, H, d, d]."""
+    q = np.asarray(q, np.float64)
+    H, T, d = q.shape
+    cu = np.asarray(cu_seqlens, np.int64)
+    nseq = len(cu) - 1
+    off = np.zeros(nseq, np.int64) if pos_offset is None else np.asarray(pos_offset, np.int64)
+    o = np.zeros(q.shape)
+    Sf = np.zeros((nseq, H, d, d))
+    for s_ in range(nseq):
+        a, e = cu[s_], cu[s_ + 1]
+        pos = off[s_] + np.arange(e - a)
+        for h in range(H):
+            qr = rope(q[h, a:e], pos, rope_dims, base)
+            kr = rope(k[h, a:e], pos, rope_dims, base)
+            o[h, a:e], Sf[s_, h] = masked_state_form(qr, kr, v[h, a:e],
+                                                      None if S0 is None else S0[s_, h])
+    return o, Sf
+
+
+def decode_rope(q, k, v, S0, positions, rope_dims: int, base: float):
+    """Decode steps with rotated q and k: q, k, v [steps, units, d], S0 [units,
+    d, d], positions [units] of the first step (step t is at positions + t).
+    Returns (o, S_final) in float64."""
+    q = np.asarray(q, np.float64)
+    steps, units, d = q.shape
+    S = np.array(S0, np.float64).reshape(units, d, d).copy()
+    o = np.zeros((steps, units, d))
+    pos0 = np.asarray(positions, np.int64)
+    for t in range(steps):
+        for u in range(units):
+            qr = rope(q[t, u][None], [pos0[u] + t], rope_dims, base)[0]
+            kr = rope(k[t, u][None], [pos0[u] + t], rope_dims, base)[0]
+            o[t, u] = qr @ S[u]
+            S[u] += np.outer(kr, np.asarray(v[t, u], np.float64))
     return o, S
 
 

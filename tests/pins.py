@@ -12,6 +12,9 @@ Implementation signatures:
     dec(q, k, v, S0) -> (o, S_final)     q, k, v: [steps, units, d], S0 [units, d, d]
     varlen(q, k, v, cu) -> o             q, k, v: [heads, T, d]
     stf(q, k, v, S0) -> (o, S_final)     one [n, d] unit continued from S0 [d, d]
+    rope(x, positions, rope_dims, base)  x [n, d] rotated at integer positions [n]
+    ratt(q, k, v, p0, S0) -> (o, S_final)  one [n, d] unit, q and k rotated at
+                                         positions p0 + t (rope_dims, base bound)
 """
 import json
 import os
@@ -236,3 +239,106 @@ def check_state_exact(stf, n=9, d=3, seed=41):
     o, Sf = stf(q, k, v, S0)
     assert np.array_equal(np.asarray(o), np.asarray(exp, np.float64))
     assert np.array_equal(np.asarray(Sf), np.asarray([[float(x) for x in row] for row in S]))
+
+
+# ---- rotary position embedding (rope_dims of d rotated, split-half pairs) --
+
+def check_golden_rope(rope):
+    """Hand-worked rotation at positions 1 and 2 (tests/golden)."""
+    g = load_golden("hand_rope_d6_r4.json")
+    x = np.asarray([g["x"], g["x"]], np.float64)
+    y = np.asarray(rope(x, np.asarray(g["positions"]), g["rope_dims"], g["base"]))
+    assert np.allclose(y, np.asarray(g["y"]), rtol=0, atol=1e-15)
+
+
+def check_rope_complex(rope, n=40, d=12, r=8, base=10000.0, seed=51, tol=1e-13):
+    """Library routine: pair i read as the complex number x_i + 1j x_{i+r/2}
+    is multiplied by exp(1j p w_i); dims from r on are unchanged."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, d))
+    pos = rng.integers(0, 1 << 20, size=n)
+    y = np.asarray(rope(x, pos, r, base))
+    h = r // 2
+    w = np.power(float(base), -np.arange(h) * 2.0 / r)
+    z = (x[:, :h] + 1j * x[:, h:r]) * np.exp(1j * (pos[:, None] * w))
+    assert np.allclose(y[:, :h], z.real, rtol=0, atol=tol * 4)
+    assert np.allclose(y[:, h:r], z.imag, rtol=0, atol=tol * 4)
+    assert np.array_equal(y[:, r:], x[:, r:])
+
+
+def check_rope_frequencies(rope, r=64, base=10000.0):
+    """Closed form: a unit vector e_i at position 1 turns by w_i, with
+    w_0 = 1, w_{r/4} = 1/sqrt(base), w_{r/2-1} = base^(-(r-2)/r) and a
+    constant ratio w_{i+1} / w_i = base^(-2/r)."""
+    h = r // 2
+    x = np.eye(r)[:h]
+    y = np.asarray(rope(x, np.ones(h, np.int64), r, base))
+    w = np.array([np.arctan2(y[i, i + h], y[i, i]) for i in range(h)])
+    assert abs(w[0] - 1.0) < 1e-15
+    assert abs(w[h // 2] - 1.0 / np.sqrt(base)) < 1e-15
+    assert abs(w[h - 1] - base ** (-(r - 2) / r)) < 1e-15
+    assert np.allclose(w[1:] / w[:-1], base ** (-2.0 / r), rtol=1e-12, atol=0)
+
+
+def check_rope_invariants(rope, n=33, d=10, r=6, base=500.0, seed=53, tol=1e-12):
+    """Invariants: position 0 is the identity; each pair keeps its norm;
+    R_p R_s = R_{p+s}; <R_p a, R_s b> depends only on p - s."""
+    rng = np.random.default_rng(seed)
+    a, b = rng.standard_normal((n, d)), rng.standard_normal((n, d))
+    assert np.array_equal(np.asarray(rope(a, np.zeros(n, np.int64), r, base)), a)
+    p = rng.integers(0, 5000, size=n)
+    s = rng.integers(0, 5000, size=n)
+    ya = np.asarray(rope(a, p, r, base))
+    h = r // 2
+    assert np.allclose(ya[:, :h] ** 2 + ya[:, h:r] ** 2, a[:, :h] ** 2 + a[:, h:r] ** 2,
+                       rtol=0, atol=tol * 10)
+    assert np.allclose(np.asarray(rope(ya, s, r, base)), np.asarray(rope(a, p + s, r, base)),
+                       rtol=0, atol=1e-9)
+    yb = np.asarray(rope(b, s, r, base))
+    c = 777
+    dot1 = np.sum(ya * yb, axis=1)
+    dot2 = np.sum(np.asarray(rope(a, p + c, r, base)) * np.asarray(rope(b, s + c, r, base)), axis=1)
+    assert np.allclose(dot1, dot2, rtol=0, atol=1e-9)
+
+
+def check_rope_attention(ratt, rope_dims, base, n=37, d=8, p0=1000, seed=57, tol=1e-10):
+    """Brute force in complex form: with S0 = 0, o_t = sum_{j<=t} score(t, j) v_j
+    where score = sum_{a>=r} q_ta k_ja + Re sum_i conj(zq_ti) zk_ji exp(1j (j-t) w_i)
+    (a function of t - j only, so o does not depend on p0), and S_final =
+    sum_j (R_{p0+j} k_j)^T v_j."""
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((n, d)).astype(np.float32) for _ in range(3))
+    q64, k64, v64 = (x.astype(np.float64) for x in (q, k, v))
+    r, h = rope_dims, rope_dims // 2
+    w = np.power(float(base), -np.arange(h) * 2.0 / r)
+    zq = q64[:, :h] + 1j * q64[:, h:r]
+    zk = k64[:, :h] + 1j * k64[:, h:r]
+    ref = np.zeros((n, d))
+    for t in range(n):
+        for j in range(t + 1):
+            sc = q64[t, r:] @ k64[j, r:] + np.sum(np.conj(zq[t]) * zk[j] * np.exp(1j * (j - t) * w)).real
+            ref[t] += sc * v64[j]
+    zr = zk * np.exp(1j * np.outer(p0 + np.arange(n), w))
+    kr = np.concatenate([zr.real, zr.imag, k64[:, r:]], axis=1)
+    sref = kr.T @ v64
+    for off in (p0, 0, 65536):
+        o, Sf = ratt(q, k, v, off, None)
+        assert np.allclose(o, ref, rtol=0, atol=tol * np.abs(ref).max())
+        if off == p0:
+            assert np.allclose(Sf, sref, rtol=0, atol=tol * np.abs(sref).max())
+
+
+def check_rope_resume(ratt, n=70, d=8, cuts=(1, 16, 33, 69), p0=5, seed=59, tol=1e-10):
+    """Invariant: a unit run in two pieces, the second continued from the
+    first's final state at positions that continue the first's, equals the
+    run in one piece."""
+    rng = np.random.default_rng(seed)
+    q, k, v = (rng.standard_normal((n, d)).astype(np.float32) for _ in range(3))
+    S0 = rng.standard_normal((d, d))
+    o, Sf = ratt(q, k, v, p0, S0)
+    for m in cuts:
+        o1, S1 = ratt(q[:m], k[:m], v[:m], p0, S0)
+        o2, S2 = ratt(q[m:], k[m:], v[m:], p0 + m, S1)
+        oo = np.concatenate([np.asarray(o1), np.asarray(o2)])
+        assert np.allclose(oo, o, rtol=0, atol=tol * np.abs(o).max())
+        assert np.allclose(S2, Sf, rtol=0, atol=tol * np.abs(Sf).max())

@@ -166,6 +166,61 @@ def test_state_batched_and_varlen(O):
     assert np.array_equal(o0, O.causal_linear_attention_varlen(qp, kp, vp, cu))
 
 
+def test_rope(O):
+    pins.check_golden_rope(O.rope)
+    pins.check_rope_complex(O.rope)
+    pins.check_rope_frequencies(O.rope)
+    pins.check_rope_frequencies(O.rope, r=64, base=1e7)
+    pins.check_rope_invariants(O.rope)
+
+
+def ratt(O, r=4, base=100.0):
+    def f(q, k, v, p0, S0):
+        o, Sf = O.causal_linear_attention_rope(q[None, None], k[None, None], v[None, None], r,
+                                               base, [p0], None if S0 is None else S0[None, None])
+        return o[0, 0], Sf[0, 0]
+    return f
+
+
+def test_rope_attention(O):
+    for r, base in ((4, 100.0), (8, 10000.0), (2, 3.0)):
+        pins.check_rope_attention(ratt(O, r, base), r, base)
+        pins.check_rope_resume(ratt(O, r, base))
+
+
+def test_rope_attention_varlen_and_decode(O):
+    """Packed sequences restart their positions (plus their offset) at each
+    sequence's first token; decode at positions continuing a prefill matches
+    the prefill of the whole."""
+    rng = np.random.default_rng(61)
+    lengths = [7, 0, 12, 1]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T, H, d, r, base = int(cu[-1]), 2, 8, 4, 50.0
+    q, k, v = (rng.standard_normal((H, T, d)).astype(np.float32) for _ in range(3))
+    off = np.array([0, 9, 100, 3])
+    S0 = rng.standard_normal((4, H, d, d))
+    o, Sf = O.causal_linear_attention_rope_varlen(q, k, v, cu, r, base, off, S0)
+    for s_ in range(4):
+        a, e = cu[s_], cu[s_ + 1]
+        od, Sd = O.causal_linear_attention_rope(q[None, :, a:e], k[None, :, a:e], v[None, :, a:e],
+                                                r, base, [off[s_]], S0[s_][None])
+        assert np.array_equal(o[:, a:e], od[0]) and np.array_equal(Sf[s_], Sd[0])
+    assert np.array_equal(Sf[1], S0[1])
+    # decode continuing a prefill of 11 tokens
+    n, m = 16, 11
+    qd, kd, vd = (rng.standard_normal((1, H, n, d)).astype(np.float32) for _ in range(3))
+    ofull, Sfull = O.causal_linear_attention_rope(qd, kd, vd, r, base, [4])
+    _, Sm = O.causal_linear_attention_rope(qd[:, :, :m], kd[:, :, :m], vd[:, :, :m], r, base, [4])
+    steps = lambda x: np.transpose(x[0, :, m:], (1, 0, 2))
+    od, Sd = O.decode_rope(steps(qd), steps(kd), steps(vd), Sm[0], np.full(H, 4 + m), r, base)
+    # a decode step reads the state before its token; the token's own term is
+    # (R_p q . R_p k) v = (q . k) v since both turn by the same angles
+    own = np.sum(qd[0, :, m:].astype(np.float64) * kd[0, :, m:], axis=-1)[..., None] * vd[0, :, m:]
+    assert np.allclose(np.transpose(od, (1, 0, 2)) + own, ofull[0, :, m:], rtol=0,
+                       atol=1e-12 * np.abs(ofull).max())
+    assert np.allclose(Sd, Sfull[0], rtol=0, atol=1e-12 * np.abs(Sfull).max())
+
+
 # ------------------------------------------------- mutants: the pins must bite
 
 def _np_causal(q, k, v, strict=False, transpose_state=False):
@@ -288,3 +343,64 @@ def test_mutants_are_caught():
     no_carry = lambda q, k, v, S0: _np_state(q, k, v, S0, final_without_s0=True)
     assert _fails(pins.check_golden_state, no_carry)
     assert _fails(pins.check_state_resume, no_carry)
+
+
+def _np_rope(x, pos, r, base, interleaved=False, negative=False, over_d=False, shift=0, all_dims=False):
+    x = np.asarray(x, np.float64)
+    r = x.shape[-1] if all_dims else r
+    h = r // 2
+    den = x.shape[-1] * 2 if over_d else r
+    w = float(base) ** (-2.0 * (np.arange(h) + shift) / den)
+    ang = np.asarray(pos, np.float64)[..., None] * w * (-1 if negative else 1)
+    c, sn = np.cos(ang), np.sin(ang)
+    y = x.copy()
+    ia = np.arange(0, r, 2) if interleaved else np.arange(h)
+    ib = ia + 1 if interleaved else ia + h
+    y[..., ia] = x[..., ia] * c - x[..., ib] * sn
+    y[..., ib] = x[..., ia] * sn + x[..., ib] * c
+    return y
+
+
+def _np_ratt(r, base, rot_v=False, q_only=False, ignore_p0=False):
+    def f(q, k, v, p0, S0):
+        n, d = q.shape
+        pos = (0 if ignore_p0 else p0) + np.arange(n)
+        qr = _np_rope(q, pos, r, base)
+        kr = k.astype(np.float64) if q_only else _np_rope(k, pos, r, base)
+        vr = _np_rope(v, pos, r, base) if rot_v else v.astype(np.float64)
+        return _np_state(qr, kr, vr, np.zeros((d, d)) if S0 is None else S0)
+    return f
+
+
+def test_rope_mutants_are_caught():
+    good = lambda x, p, r, b: _np_rope(x, p, r, b)
+    pins.check_golden_rope(good)
+    pins.check_rope_complex(good)
+    pins.check_rope_frequencies(good)
+    pins.check_rope_invariants(good)
+    # adjacent (interleaved) pairs instead of split halves
+    inter = lambda x, p, r, b: _np_rope(x, p, r, b, interleaved=True)
+    assert _fails(pins.check_golden_rope, inter)
+    assert _fails(pins.check_rope_complex, inter)
+    # rotation the wrong way
+    neg = lambda x, p, r, b: _np_rope(x, p, r, b, negative=True)
+    assert _fails(pins.check_golden_rope, neg)
+    assert _fails(pins.check_rope_complex, neg)
+    assert _fails(pins.check_rope_frequencies, neg)
+    # exponent over the whole head dim, or frequencies off by one pair
+    overd = lambda x, p, r, b: _np_rope(x, p, r, b, over_d=True)
+    assert _fails(pins.check_golden_rope, overd)
+    assert _fails(pins.check_rope_frequencies, overd)
+    off1 = lambda x, p, r, b: _np_rope(x, p, r, b, shift=1)
+    assert _fails(pins.check_golden_rope, off1)
+    assert _fails(pins.check_rope_frequencies, off1)
+    # every dim rotated
+    alld = lambda x, p, r, b: _np_rope(x, p, r, b, all_dims=True)
+    assert _fails(pins.check_golden_rope, alld)
+    assert _fails(pins.check_rope_complex, alld)
+    # attention: the oracle-shaped good variant passes, the mistakes fail
+    pins.check_rope_attention(_np_ratt(4, 100.0), 4, 100.0)
+    pins.check_rope_resume(_np_ratt(4, 100.0))
+    assert _fails(pins.check_rope_attention, _np_ratt(4, 100.0, rot_v=True), 4, 100.0)
+    assert _fails(pins.check_rope_attention, _np_ratt(4, 100.0, q_only=True), 4, 100.0)
+    assert _fails(pins.check_rope_resume, _np_ratt(4, 100.0, ignore_p0=True))
