@@ -147,9 +147,11 @@ def bench_prefill(w, steps, warmup, dev, traced=True):
     return (t1 - t0) * 1000.0 / steps, stage, chunk, nbytes
 
 
-def bench_prefill_state(w, steps, warmup, dev):
+def bench_prefill_state(w, steps, warmup, dev, rope=False):
     """The prefill workload through lightning_attn_fwd_state, each sequence
-    starting from a state and returning its final state (in place)."""
+    starting from a state and returning its final state (in place); with
+    rope, through lightning_attn_fwd_rope instead (q and k rotated on half
+    the head dims, base 10,000, positions from 0, no states)."""
     import torch
     import linear_attention_attn_amd as la
     import synth
@@ -164,8 +166,13 @@ def bench_prefill_state(w, steps, warmup, dev):
     stream = torch.cuda.current_stream(dev).cuda_stream
 
     def with_state():
-        st = la.lightning_attn_fwd_state(q, k, v, o, w.batch, w.heads, w.seq_len, w.head_dim,
-                                         w.block_size, None, code, S, S, ws, nbytes, stream)
+        if rope:
+            st = la.lightning_attn_fwd_rope(q, k, v, o, w.batch, w.heads, w.seq_len, w.head_dim,
+                                            w.block_size, None, code, w.head_dim // 2, 1e4, None,
+                                            None, None, ws, nbytes, stream)
+        else:
+            st = la.lightning_attn_fwd_state(q, k, v, o, w.batch, w.heads, w.seq_len, w.head_dim,
+                                             w.block_size, None, code, S, S, ws, nbytes, stream)
         if st != la.LA_OK:
             raise la.LightningAttnError(st, "lightning_attn_fwd_state")
 
@@ -450,6 +457,14 @@ def main():
             "state_bytes": w.batch * w.heads * 2 * 4 * d * d,
             "overhead_vs_plain": sms / pms - 1.0}
         log(json.dumps(out["state_handoff"]))
+        rms, pms = bench_prefill_state(w, args.steps, args.warmup, dev, rope=True)
+        out["rope"] = {
+            "workload": f"{w.name} through lightning_attn_fwd_rope: q and k rotated on the first "
+                        "64 of 128 dims (base 10,000) inside the kernels",
+            "ms_per_step": rms, "tokens_per_s": tokens / (rms * 1e-3),
+            "ms_per_step_plain_same_timing": pms,
+            "overhead_vs_plain": rms / pms - 1.0}
+        log(json.dumps(out["rope"]))
         wl = synth.WORKLOADS["long_1m"]
         log(f"prefill {wl.name}: {wl.note}")
         lms, lstage, lchunk, _ = bench_prefill(wl, 5, 3, dev)

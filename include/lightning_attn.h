@@ -173,6 +173,47 @@ int lightning_attn_decode_indexed(const void *q, const void *k, const void *v, f
                                   int nslots, const int32_t *slots, void *o, int batch, int heads,
                                   int head_dim, int dtype, void *stream);
 
+/*
+ * lightning_attn_fwd_state with rotary position embedding applied to q and k
+ * on the way in (wiki page "MiniMax-01 Lightning Attention", section
+ * "模型架构": RoPE on half of each head's dims, base frequency 10,000, raised
+ * to 10M for the long-context stage).  The page leaves the details open;
+ * this library takes: the first rope_dims dims are rotated, dim i
+ * (i < rope_dims / 2) paired with dim i + rope_dims / 2, the pair at position
+ * p turned by the angle p * rope_base^(-2i / rope_dims); v is not rotated.
+ *   rope_dims:  must equal head_dim / 2 (else LA_EUNSUPPORTED);
+ *   rope_base:  > 0 and finite (else LA_EINVAL);
+ *   pos_offset: NULL (every sequence's first token is at position 0) or a
+ *               DEVICE int32 [batch]: token t of sequence s is at position
+ *               pos_offset[s] + t (a sequence continued from a handed-over
+ *               state continues its positions).
+ * q and k are read only (the rotation happens in registers and LDS).  The
+ * final state is that of the rotated keys, the state a rotated decode step
+ * (lightning_attn_decode_rope) continues.  dtype must be LA_DTYPE_BF16 (else
+ * LA_EUNSUPPORTED).  Everything else is as lightning_attn_fwd_state.
+ */
+int lightning_attn_fwd_rope(const void *q, const void *k, const void *v, void *o,
+                            int batch, int heads, int64_t seq_len, int head_dim, int block_size,
+                            const int32_t *cu_seqlens, int dtype,
+                            int rope_dims, double rope_base, const int32_t *pos_offset,
+                            const float *s_init, float *s_final,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step with q and k rotated as in lightning_attn_fwd_rope, row b
+ * at position positions[b] (DEVICE int32 [batch], required).  With slots ==
+ * NULL the states are [batch][heads][head_dim][head_dim] (as
+ * lightning_attn_decode; nslots is ignored); otherwise row b uses pool entry
+ * slots[b] of a pool of nslots entries, with padding rows, as
+ * lightning_attn_decode_indexed.  rope_dims must equal head_dim / 2;
+ * dtype LA_DTYPE_BF16 or LA_DTYPE_F32.  o = (R q) . S_old,
+ * S_new = S_old + (R k)^T v.
+ */
+int lightning_attn_decode_rope(const void *q, const void *k, const void *v, float *state,
+                               int nslots, const int32_t *slots, void *o, int batch, int heads,
+                               int head_dim, int dtype, int rope_dims, double rope_base,
+                               const int32_t *positions, void *stream);
+
 /* Static, human-readable text for a status code. */
 const char *lightning_attn_strerror(int status);
 

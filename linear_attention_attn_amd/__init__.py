@@ -22,7 +22,8 @@ __all__ = [
     "LA_EHIP", "LightningAttnError", "lib_path", "load_library",
     "lightning_attn_fwd_workspace_size", "lightning_attn_fwd_chunk_tokens", "lightning_attn_fwd",
     "lightning_attn_fwd_traced", "lightning_attn_decode", "lightning_attn_strerror", "fwd",
-    "decode", "LA_FWD_NUM_EVENTS",
+    "decode", "LA_FWD_NUM_EVENTS", "lightning_attn_fwd_state", "lightning_attn_fwd_rope",
+    "lightning_attn_decode_indexed", "lightning_attn_decode_rope", "decode_indexed", "decode_rope",
 ]
 
 LA_DTYPE_BF16 = 0
@@ -71,6 +72,12 @@ def load_library():
     lib.lightning_attn_decode.restype = i32
     lib.lightning_attn_decode_indexed.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, vp]
     lib.lightning_attn_decode_indexed.restype = i32
+    lib.lightning_attn_fwd_rope.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, i32, i32,
+                                            ctypes.c_double, vp, vp, vp, vp, sz, vp]
+    lib.lightning_attn_fwd_rope.restype = i32
+    lib.lightning_attn_decode_rope.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
+                                               ctypes.c_double, vp, vp]
+    lib.lightning_attn_decode_rope.restype = i32
     lib.lightning_attn_strerror.argtypes = [i32]
     lib.lightning_attn_strerror.restype = ctypes.c_char_p
     _LIB = lib
@@ -113,6 +120,15 @@ def lightning_attn_fwd_state(q, k, v, o, batch, heads, seq_len, head_dim, block_
         stream))
 
 
+def lightning_attn_fwd_rope(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens,
+                            dtype, rope_dims, rope_base, pos_offset, s_init, s_final, workspace,
+                            workspace_bytes, stream) -> int:
+    return int(load_library().lightning_attn_fwd_rope(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, heads, seq_len, head_dim, block_size,
+        _ptr(cu_seqlens), dtype, rope_dims, float(rope_base), _ptr(pos_offset), _ptr(s_init),
+        _ptr(s_final), _ptr(workspace), workspace_bytes, stream))
+
+
 def lightning_attn_fwd_traced(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens,
                               dtype, workspace, workspace_bytes, stream, events, nevents) -> int:
     arr = (ctypes.c_void_p * max(1, len(events)))(*events) if events is not None else None
@@ -131,6 +147,13 @@ def lightning_attn_decode_indexed(q, k, v, state_pool, nslots, slots, o, batch, 
     return int(load_library().lightning_attn_decode_indexed(
         _ptr(q), _ptr(k), _ptr(v), _ptr(state_pool), nslots, _ptr(slots), _ptr(o), batch, heads,
         head_dim, dtype, stream))
+
+
+def lightning_attn_decode_rope(q, k, v, state, nslots, slots, o, batch, heads, head_dim, dtype,
+                               rope_dims, rope_base, positions, stream) -> int:
+    return int(load_library().lightning_attn_decode_rope(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(state), nslots, _ptr(slots), _ptr(o), batch, heads,
+        head_dim, dtype, rope_dims, float(rope_base), _ptr(positions), stream))
 
 
 def lightning_attn_strerror(status: int) -> str:
@@ -167,7 +190,8 @@ def workspace_for(q, block_size: int, cu_seqlens=None):
 
 
 def fwd(q, k, v, block_size: int = 256, cu_seqlens=None, out=None, workspace=None,
-        s_init=None, s_final=None):
+        s_init=None, s_final=None, rope_dims: int = 0, rope_base: float = 10000.0,
+        pos_offset=None):
     """Causal linear attention forward on the current stream.
 
     Dense: q, k, v [batch, heads, n, d].  Packed: q, k, v [heads, T, d] with
@@ -176,6 +200,9 @@ def fwd(q, k, v, block_size: int = 256, cu_seqlens=None, out=None, workspace=Non
     (nseq = batch for dense input): the state each sequence starts from, and
     the tensor that receives each sequence's state after its last token (it
     may be s_init itself).
+    rope_dims > 0 (= d / 2, bf16 only): q and k rotated on the way in
+    (lightning_attn_fwd_rope), token t of sequence s at position
+    pos_offset[s] + t (pos_offset: int32 device tensor [nseq], or None for 0).
     """
     import torch
     for t in (q, k, v):
@@ -201,7 +228,14 @@ def fwd(q, k, v, block_size: int = 256, cu_seqlens=None, out=None, workspace=Non
         if x is not None and (x.dtype != torch.float32 or not x.is_contiguous() or not x.is_cuda
                               or tuple(x.shape) != (batch, heads, d, d)):
             raise ValueError("s_init / s_final must be contiguous fp32 device tensors [nseq, heads, d, d]")
-    if s_init is None and s_final is None:
+    if pos_offset is not None and (pos_offset.dtype != torch.int32 or not pos_offset.is_cuda
+                                   or pos_offset.numel() != batch):
+        raise ValueError("pos_offset must be an int32 device tensor of nseq entries")
+    if rope_dims:
+        st = lightning_attn_fwd_rope(q, k, v, o, batch, heads, n, d, block_size, cu, _dtype_code(q),
+                                     rope_dims, rope_base, pos_offset, s_init, s_final,
+                                     workspace if nbytes else None, nbytes, _stream_handle(q.device))
+    elif s_init is None and s_final is None:
         st = lightning_attn_fwd(q, k, v, o, batch, heads, n, d, block_size, cu, _dtype_code(q),
                                 workspace if nbytes else None, nbytes, _stream_handle(q.device))
     else:
@@ -254,4 +288,36 @@ def decode_indexed(q, k, v, state_pool, slots, out=None):
                                        _dtype_code(q), _stream_handle(q.device))
     if st != LA_OK:
         raise LightningAttnError(st, "lightning_attn_decode_indexed")
+    return o
+
+
+def decode_rope(q, k, v, state, positions, rope_dims: int, rope_base: float = 10000.0, slots=None,
+                out=None):
+    """One decode step with q and k rotated at positions[b] (int32 device
+    tensor [batch]).  Without slots: state fp32 [batch, heads, d, d]; with
+    slots (int32 device [batch]): state is a pool [nslots, heads, d, d] as in
+    decode_indexed.
+    """
+    import torch
+    if state.dtype != torch.float32 or not state.is_contiguous():
+        raise ValueError("state must be a contiguous fp32 tensor")
+    batch, heads, d = q.shape
+    if positions.dtype != torch.int32 or not positions.is_cuda or positions.numel() != batch:
+        raise ValueError("positions must be an int32 device tensor of batch entries")
+    if slots is None:
+        if tuple(state.shape) != (batch, heads, d, d):
+            raise ValueError("state shape must be [batch, heads, d, d]")
+        nslots = 0
+    else:
+        if tuple(state.shape[1:]) != (heads, d, d):
+            raise ValueError("state pool shape must be [nslots, heads, d, d]")
+        if slots.dtype != torch.int32 or not slots.is_cuda or slots.numel() != batch:
+            raise ValueError("slots must be an int32 device tensor of batch entries")
+        nslots = state.shape[0]
+    o = torch.empty_like(q) if out is None else out
+    st = lightning_attn_decode_rope(q, k, v, state, nslots, slots, o, batch, heads, d,
+                                    _dtype_code(q), rope_dims, rope_base, positions,
+                                    _stream_handle(q.device))
+    if st != LA_OK:
+        raise LightningAttnError(st, "lightning_attn_decode_rope")
     return o

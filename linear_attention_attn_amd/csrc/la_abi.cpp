@@ -4,6 +4,7 @@
 // before any HIP call, so a rejected call has no side effects.  The library
 // allocates nothing: the caller passes all device memory, including the
 // workspace sized by lightning_attn_fwd_workspace_size.
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 
@@ -119,11 +120,23 @@ int64_t lightning_attn_fwd_chunk_tokens(int batch, int heads, int64_t seq_len, i
     return p.chunk;
 }
 
+// Rotary arguments: rope_dims 0 (none) or head_dim / 2 with a finite base > 0.
+static int check_rope(int rope_dims, double rope_base, int head_dim) {
+    if (rope_dims == 0) return LA_OK;
+    if (rope_dims != head_dim / 2) return LA_EUNSUPPORTED;
+    if (!(rope_base > 0.0) || !isfinite(rope_base)) return LA_EINVAL;
+    return LA_OK;
+}
+
 static int fwd_common(const void *q, const void *k, const void *v, void *o, int batch, int heads,
                       int64_t seq_len, int head_dim, int block_size, const int32_t *cu_seqlens,
                       int dtype, const float *s_init, float *s_final, void *workspace,
-                      size_t workspace_bytes, void *stream, void *const *events) {
+                      size_t workspace_bytes, void *stream, void *const *events,
+                      int rope_dims = 0, double rope_base = 0.0, const int32_t *pos0 = nullptr) {
     int st = la::check_fwd_shape(batch, heads, seq_len, head_dim, block_size, dtype);
+    if (st != LA_OK) return st;
+    if (rope_dims != 0 && dtype != LA_DTYPE_BF16) return LA_EUNSUPPORTED;
+    st = check_rope(rope_dims, rope_base, head_dim);
     if (st != LA_OK) return st;
     if (((uintptr_t)s_init & 15) != 0 || ((uintptr_t)s_final & 15) != 0) return LA_EINVAL;
     if (seq_len == 0) {
@@ -137,6 +150,7 @@ static int fwd_common(const void *q, const void *k, const void *v, void *o, int 
     a.nseq = batch; a.heads = heads; a.head_dim = head_dim; a.block_size = block_size;
     a.dtype = dtype; a.seq_len = seq_len; a.cu_seqlens = cu_seqlens;
     a.s_init = s_init; a.s_final = s_final;
+    a.rope_dims = rope_dims; a.rope_base = rope_base; a.pos0 = pos0;
     la::make_fwd_plan(batch, heads, seq_len, head_dim, block_size, cu_seqlens != nullptr, &a.plan);
     if (!workspace || workspace_bytes < a.plan.bytes) return LA_EWORKSPACE;
     if (((uintptr_t)workspace & 255) != 0) return LA_EINVAL;
@@ -158,6 +172,17 @@ int lightning_attn_fwd_state(const void *q, const void *k, const void *v, void *
                              void *stream) {
     return fwd_common(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens, dtype,
                       s_init, s_final, workspace, workspace_bytes, stream, nullptr);
+}
+
+int lightning_attn_fwd_rope(const void *q, const void *k, const void *v, void *o, int batch,
+                            int heads, int64_t seq_len, int head_dim, int block_size,
+                            const int32_t *cu_seqlens, int dtype, int rope_dims, double rope_base,
+                            const int32_t *pos_offset, const float *s_init, float *s_final,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    if (rope_dims <= 0) return LA_EUNSUPPORTED;
+    return fwd_common(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens, dtype,
+                      s_init, s_final, workspace, workspace_bytes, stream, nullptr, rope_dims,
+                      rope_base, pos_offset);
 }
 
 int lightning_attn_fwd_traced(const void *q, const void *k, const void *v, void *o, int batch,
@@ -193,6 +218,30 @@ int lightning_attn_decode_indexed(const void *q, const void *k, const void *v, f
     if (!q || !k || !v || !slots || !o || (nslots > 0 && !state_pool)) return LA_EINVAL;
     return la::launch_decode(q, k, v, state_pool, o, batch, heads, head_dim, dtype, stream, slots,
                              nslots) == 0 ? LA_OK : LA_EHIP;
+}
+
+int lightning_attn_decode_rope(const void *q, const void *k, const void *v, float *state, int nslots,
+                               const int32_t *slots, void *o, int batch, int heads, int head_dim,
+                               int dtype, int rope_dims, double rope_base, const int32_t *positions,
+                               void *stream) {
+    if (!(dtype == LA_DTYPE_BF16 || dtype == LA_DTYPE_F32)) return LA_EUNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return LA_EUNSUPPORTED;
+    if (rope_dims <= 0) return LA_EUNSUPPORTED;
+    const int rs = check_rope(rope_dims, rope_base, head_dim);
+    if (rs != LA_OK) return rs;
+    if (batch < 1 || heads < 1) return LA_EINVAL;
+    if ((int64_t)batch * heads > (int64_t)INT32_MAX) return LA_EUNSUPPORTED;
+    if (!q || !k || !v || !o || !positions) return LA_EINVAL;
+    if (slots) {
+        if (nslots < 0) return LA_EINVAL;
+        if ((int64_t)nslots * heads > (int64_t)INT32_MAX) return LA_EUNSUPPORTED;
+        if (nslots > 0 && !state) return LA_EINVAL;
+    } else {
+        if (!state) return LA_EINVAL;
+        nslots = 0;
+    }
+    return la::launch_decode(q, k, v, state, o, batch, heads, head_dim, dtype, stream, slots, nslots,
+                             rope_dims, rope_base, positions) == 0 ? LA_OK : LA_EHIP;
 }
 
 const char *lightning_attn_strerror(int status) {

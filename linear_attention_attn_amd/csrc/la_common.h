@@ -269,6 +269,74 @@ __device__ __forceinline__ void hold(const F (&f)[N]) {
 // bound how many operand fragments are live at once).
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 
+// ---- rotary position embedding (bf16 operands) ---------------------------
+// Pair i of a token at position pos turns by the angle pos * theta_i with
+// theta_i = base^(-2i / r) (r rotated dims; pair i is dims i and i + r/2).
+// The angle is kept in turns: t = frac(pos * f_i) with f_i = theta_i / (2 pi).
+// Positions reach millions, so the product and its fractional part are taken
+// in fp64; the sine and cosine of the turn fraction come from the hardware's
+// v_sin_f32 / v_cos_f32, which take their argument in turns.  Consecutive
+// pairs' frequencies differ by the factor rho = base^(-2/r).
+
+// rho = base^(-2/r), the ratio f_{i+1} / f_i.
+__device__ __forceinline__ double rope_rho(double base, int r) { return exp2(-2.0 / r * log2(base)); }
+
+// f_{i0} = rho^{i0} / (2 pi) for i0 a multiple of 8 below 64, from rho8 = rho^8.
+__device__ __forceinline__ double rope_f(int i0, double rho8) {
+    double f = 0.5 / 3.14159265358979323846;
+#pragma unroll
+    for (int j = 1; j < 8; ++j)
+        if (8 * j <= i0) f *= rho8;
+    return f;
+}
+
+__device__ __forceinline__ void rope_cs(double pos, double f, float &c, float &s) {
+    double t = pos * f;
+    t -= floor(t);
+    const float tf = (float)t;
+    s = __builtin_amdgcn_sinf(tf);
+    c = __builtin_amdgcn_cosf(tf);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Rotate the eight pairs (x[e], y[e]), e = 0..7, of pairs i0 + e (f = f_{i0})
+// at position pos; x holds the first dims of the pairs, y their partners.
+__device__ __forceinline__ void rope_rot8(u32x4_t &x, u32x4_t &y, double pos, double f, double rho) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        float c0, s0, c1, s1;
+        rope_cs(pos, f, c0, s0);
+        f *= rho;
+        rope_cs(pos, f, c1, s1);
+        f *= rho;
+        const float x0 = bf16_lo(x[d]), x1 = bf16_hi(x[d]), y0 = bf16_lo(y[d]), y1 = bf16_hi(y[d]);
+        x[d] = pack_bf16x2(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+        y[d] = pack_bf16x2(x0 * s0 + y0 * c0, x1 * s1 + y1 * c1);
+    }
+}
+
+// One side of eight pairs whose two halves sit in different lanes: `mine`
+// becomes its rotated self, given the partner's values `other`; `first` says
+// whether `mine` holds the pairs' first dims.
+__device__ __forceinline__ u32x4_t rope_rot8_half(const u32x4_t &mine, const u32x4_t &other, bool first,
+                                                  double pos, double f, double rho) {
+    u32x4_t r;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        float c0, s0, c1, s1;
+        rope_cs(pos, f, c0, s0);
+        f *= rho;
+        rope_cs(pos, f, c1, s1);
+        f *= rho;
+        if (first) { s0 = -s0; s1 = -s1; }
+        r[d] = pack_bf16x2(bf16_lo(mine[d]) * c0 + bf16_lo(other[d]) * s0,
+                           bf16_hi(mine[d]) * c1 + bf16_hi(other[d]) * s1);
+    }
+    return r;
+}
+
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63u; }
 // The lane id produced afresh at each call (opaque to the optimiser): values
 // derived from it are recomputed where they are used instead of being held in

@@ -32,11 +32,15 @@ __device__ __forceinline__ void from_f32(float x, bf16_t *p) { p->bits = (uint16
 // their states stay in a pool): row b's state is pool entry slots[b]; rows
 // whose slot is negative or not below `nslots` are padding: their o is
 // zero and no state is touched (so a batch can be padded to a fixed size).
-template <typename T, int D>
+// With ROPE the first rope_dims dims of q and k are rotated at the row's
+// position positions[b] (pair i: dims i and i + rope_dims / 2, angle
+// positions[b] * base^(-2i / rope_dims)).
+template <typename T, int D, bool ROPE>
 __global__ __launch_bounds__(kDecThreads) void k_decode(const T *__restrict__ q, const T *__restrict__ k,
                                                       const T *__restrict__ v, float *__restrict__ state,
                                                       T *__restrict__ o, const int32_t *__restrict__ slots,
-                                                      int heads, int nslots) {
+                                                      int heads, int nslots, int rope_dims, double rope_base,
+                                                      const int32_t *__restrict__ positions) {
     constexpr int CT = D / 4;                 // threads across one row (4 columns each)
     constexpr int RG = kDecThreads / CT;      // row groups
     constexpr int RPT = D / RG;               // rows per thread
@@ -62,8 +66,21 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const T *__restrict__ q,
     }
     float *S = state + su * (int64_t)D * D;
     if (t < D) {
-        sq[t] = to_f32(qu[t]);
-        sk[t] = to_f32(ku[t]);
+        float qx = to_f32(qu[t]), kx = to_f32(ku[t]);
+        if (ROPE && t < rope_dims) {
+            const int half = rope_dims / 2;
+            const bool first = t < half;
+            const int i = first ? t : t - half, pt = first ? t + half : t - half;
+            const float qp = to_f32(qu[pt]), kp = to_f32(ku[pt]);
+            const double f = (0.5 / 3.14159265358979323846) * exp2(-2.0 * i / rope_dims * log2(rope_base));
+            float c, sn;
+            rope_cs((double)positions[unit / heads], f, c, sn);
+            if (first) sn = -sn;
+            qx = qx * c + qp * sn;
+            kx = kx * c + kp * sn;
+        }
+        sq[t] = qx;
+        sk[t] = kx;
     }
     const int c4 = t % CT, rg = t / CT;
     f32x4_t vv;
@@ -98,24 +115,34 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const T *__restrict__ q,
     }
 }
 
+template <typename T, bool ROPE>
+static void launch_dec_t(const void *q, const void *k, const void *v, float *state, void *o, int heads,
+                         int head_dim, dim3 grid, hipStream_t st, const int32_t *slots, int nslots,
+                         int rope_dims, double rope_base, const int32_t *positions) {
+    auto *qq = reinterpret_cast<const T *>(q);
+    auto *kk = reinterpret_cast<const T *>(k);
+    auto *vv = reinterpret_cast<const T *>(v);
+    auto *oo = reinterpret_cast<T *>(o);
+    if (head_dim == 64)
+        hipLaunchKernelGGL((k_decode<T, 64, ROPE>), grid, dim3(kDecThreads), 0, st, qq, kk, vv, state, oo,
+                           slots, heads, nslots, rope_dims, rope_base, positions);
+    else
+        hipLaunchKernelGGL((k_decode<T, 128, ROPE>), grid, dim3(kDecThreads), 0, st, qq, kk, vv, state, oo,
+                           slots, heads, nslots, rope_dims, rope_base, positions);
+}
+
 int launch_decode(const void *q, const void *k, const void *v, float *state, void *o, int batch,
-                  int heads, int head_dim, int dtype, void *stream, const int32_t *slots, int nslots) {
+                  int heads, int head_dim, int dtype, void *stream, const int32_t *slots, int nslots,
+                  int rope_dims, double rope_base, const int32_t *positions) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)((int64_t)batch * heads));
+    const bool rope = rope_dims > 0;
     if (dtype == 0) {
-        auto *qq = reinterpret_cast<const bf16_t *>(q);
-        auto *kk = reinterpret_cast<const bf16_t *>(k);
-        auto *vv = reinterpret_cast<const bf16_t *>(v);
-        auto *oo = reinterpret_cast<bf16_t *>(o);
-        if (head_dim == 64) hipLaunchKernelGGL((k_decode<bf16_t, 64>), grid, dim3(kDecThreads), 0, st, qq, kk, vv, state, oo, slots, heads, nslots);
-        else hipLaunchKernelGGL((k_decode<bf16_t, 128>), grid, dim3(kDecThreads), 0, st, qq, kk, vv, state, oo, slots, heads, nslots);
+        if (rope) launch_dec_t<bf16_t, true>(q, k, v, state, o, heads, head_dim, grid, st, slots, nslots, rope_dims, rope_base, positions);
+        else launch_dec_t<bf16_t, false>(q, k, v, state, o, heads, head_dim, grid, st, slots, nslots, 0, 0.0, nullptr);
     } else {
-        auto *qq = reinterpret_cast<const float *>(q);
-        auto *kk = reinterpret_cast<const float *>(k);
-        auto *vv = reinterpret_cast<const float *>(v);
-        auto *oo = reinterpret_cast<float *>(o);
-        if (head_dim == 64) hipLaunchKernelGGL((k_decode<float, 64>), grid, dim3(kDecThreads), 0, st, qq, kk, vv, state, oo, slots, heads, nslots);
-        else hipLaunchKernelGGL((k_decode<float, 128>), grid, dim3(kDecThreads), 0, st, qq, kk, vv, state, oo, slots, heads, nslots);
+        if (rope) launch_dec_t<float, true>(q, k, v, state, o, heads, head_dim, grid, st, slots, nslots, rope_dims, rope_base, positions);
+        else launch_dec_t<float, false>(q, k, v, state, o, heads, head_dim, grid, st, slots, nslots, 0, 0.0, nullptr);
     }
     return (int)hipGetLastError();
 }

@@ -42,6 +42,9 @@ struct FwdArgs {
     const int32_t *cu_seqlens;  // device, or nullptr for dense input
     const float *s_init;      // device [nseq][heads][d][d] or nullptr (zero)
     float *s_final;           // device [nseq][heads][d][d] or nullptr (not wanted)
+    int rope_dims = 0;        // > 0: rotate the first rope_dims dims of q and k (bf16)
+    double rope_base = 0.0;   // rotary base frequency
+    const int32_t *pos0 = nullptr;  // device [nseq]: position of each first token, or nullptr (0)
     char *workspace;
     FwdPlan plan;
 };
@@ -61,6 +64,7 @@ int launch_state_empty(const float *s_init, float *s_final, int nseq, int heads,
 // Returns 0 or a HIP error code.
 int launch_decode(const void *q, const void *k, const void *v, float *state, void *o,
                   int batch, int heads, int head_dim, int dtype, void *stream,
-                  const int32_t *slots = nullptr, int nslots = 0);
+                  const int32_t *slots = nullptr, int nslots = 0, int rope_dims = 0,
+                  double rope_base = 0.0, const int32_t *positions = nullptr);
 
 }  // namespace la

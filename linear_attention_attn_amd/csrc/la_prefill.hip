@@ -46,6 +46,12 @@ struct KParams {
     const float *s_init;
     float *s_final;
     int init_mode;
+    // rotary position embedding of q and k (bf16 kernels with ROPE set):
+    // rope_dims rotated dims, base frequency, and the position of each
+    // sequence's first token (pos0[s], or 0 when pos0 is nullptr)
+    const int32_t *pos0;
+    double rope_base;
+    int rope_dims;
 };
 
 // ------------------------------------------------------------------ units
@@ -710,6 +716,54 @@ struct Ring<2, SBY> {
 };
 
 
+// The 1 KiB piece filled by wave instruction gi (IPW per wave, NI pieces
+// per tensor tile, RGN 16-row groups per tile): 16 rows (row0..) of the
+// 32-element column block blk of the K (gi < NI) or V tile.  With ROPE the
+// IPW pieces of a wave are consecutive column blocks of one row group, so the
+// wave that loads column blocks 0 and 1 of a row group holds both halves of
+// every rotary pair of those rows (dims i and i + 32 for d = 128; for d = 64
+// dims i and i + 16 are both in block 0).
+template <int NI, int IPW, int RGN, bool ROPE>
+__device__ __forceinline__ void dma_piece(int gi, bool &isv, int &blk, int &row0) {
+    isv = gi >= NI;
+    const int x = isv ? gi - NI : gi;
+    if constexpr (ROPE) {
+        static_assert(NI % (IPW * RGN) == 0, "whole row groups per wave");
+        const int wk = x / IPW, ii = x % IPW;
+        blk = ii + IPW * (wk / RGN);
+        row0 = 16 * (wk % RGN);
+    } else {
+        blk = x / RGN;
+        row0 = 16 * (x % RGN);
+    }
+}
+
+// Rotary-pair frequency setup of a lane that rotates K rows of a tile: the
+// waves holding column block 0 of row group w (w < RGN) rotate rows
+// 16 w + l / 4; the lane's 16-byte chunk is logical chunk lc of its row.
+struct RopeK {
+    bool on;        // this wave rotates K pieces
+    int rowk;       // row within a tile
+    int lc;         // logical 16-byte chunk (dims 8 lc .. 8 lc + 7 of block 0)
+};
+
+template <int D, int TJ>
+__device__ __forceinline__ RopeK rope_k_lane(int w, int l) {
+    RopeK r;
+    r.on = w < TJ / 16;
+    r.rowk = 16 * w + (l >> 2);
+    r.lc = (int)((l & 3) ^ SubRows<TJ>::swz(r.rowk));
+    return r;
+}
+
+// A kernel-uniform double held in scalar registers.
+__device__ __forceinline__ double uniform_f64(double x) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // U_c = K_c^T V_c over a chunk, with the K/V tiles staged through
 // registers: each wave loads its 16-byte pieces of tile t + 2 into registers
 // (buffer loads, rows past the chunk end read as zeros) while tile t is
@@ -718,7 +772,9 @@ struct Ring<2, SBY> {
 // buffer-to-LDS loads alone stream at most ~6.3 TB/s and register loads
 // ~7.3 TB/s; this kernel does little besides streaming, and staging through
 // registers made it a little faster (about 1% on the 1M-token workload).
-template <int D, int BLK, int NW>
+//
+// With ROPE the K rows are rotated in registers before they go to LDS.
+template <int D, int BLK, int NW, bool ROPE>
 __global__ __launch_bounds__(NW * 64, 1024 / (NW * 64)) void k_summary_reg(KParams p) {
     using C = Cfg<bf16_t, D, BLK, NW>;
     constexpr int TJ = C::TJ;
@@ -760,16 +816,40 @@ __global__ __launch_bounds__(NW * 64, 1024 / (NW * 64)) void k_summary_reg(KPara
     __amdgpu_buffer_rsrc_t drs[IPW];
 #pragma unroll
     for (int ii = 0; ii < IPW; ++ii) {
-        const int gi = w * IPW + ii;
-        const bool isv = gi >= NI;
-        const int x = isv ? gi - NI : gi;
-        const int blk = x / (TJ / 16), row0 = 16 * (x % (TJ / 16));
+        bool isv;
+        int blk, row0;
+        dma_piece<NI, IPW, TJ / 16, ROPE>(w * IPW + ii, isv, blk, row0);
         const int row = row0 + (l >> 2);
         dvo[ii] = (uint32_t)(row * RB + blk * 64 + (((l & 3) ^ LT::swz(row)) << 4));
         dlo[ii] = (isv ? TB : 0) + blk * LT::BLOCK + row0 * 64 + 16 * l;
         drs[ii] = isv ? rv : rk;
     }
     u32x4_t R0[IPW], R1[IPW];
+    // rotary embedding of the K rows this lane brings (tile `tile`)
+    [[maybe_unused]] const RopeK rk_lane = rope_k_lane<D, TJ>(w, l);
+    [[maybe_unused]] double rho = 0.0, rho8 = 0.0;
+    [[maybe_unused]] int64_t pbase = 0;
+    if constexpr (ROPE) {
+        rho = uniform_f64(rope_rho(p.rope_base, p.rope_dims));
+        rho8 = uniform_f64(rho * rho * rho * rho * rho * rho * rho * rho);
+        pbase = (p.pos0 ? (int64_t)p.pos0[s] : 0) + t0;
+    }
+    auto rot = [&](u32x4_t (&R)[IPW], int tile) {
+        if constexpr (ROPE) {
+            if (rk_lane.on) {
+                const double pos = (double)(pbase + (int64_t)tile * TJ + rk_lane.rowk);
+                if constexpr (D == 128) {
+                    rope_rot8(R[0], R[1], pos, rope_f(8 * rk_lane.lc, rho8), rho);
+                } else {
+                    u32x4_t other;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)   // lane l ^ 2 holds chunk lc ^ 2 of the same row
+                        other[d] = (uint32_t)__builtin_amdgcn_mov_dpp((int)R[0][d], 0x4E, 0xF, 0xF, false);
+                    R[0] = rope_rot8_half(R[0], other, rk_lane.lc < 2, pos, rope_f(8 * (rk_lane.lc & 1), rho8), rho);
+                }
+            }
+        }
+    };
     auto load = [&](int tile, u32x4_t (&R)[IPW]) {
 #pragma unroll
         for (int ii = 0; ii < IPW; ++ii)
@@ -798,18 +878,21 @@ __global__ __launch_bounds__(NW * 64, 1024 / (NW * 64)) void k_summary_reg(KPara
     const int ntile = (n + TJ - 1) / TJ;
     load(0, R0);
     load(1, R1);
+    rot(R0, 0);
     put(stages[0], R0);
     wait_vm_lgkm0<63>();                             // own LDS writes done
     wg_barrier();
     for (int t = 0; t < ntile; t += 2) {
         load(t + 2, R0);                             // past the end: zeros, never used
         sum_tile(stages[0]);
+        rot(R1, t + 1);
         put(stages[1], R1);                          // tile t + 1 (stage 1 was last read in tile t - 1)
         wait_vm_lgkm0<63>();
         wg_barrier();
         if (t + 1 < ntile) {
             load(t + 3, R1);
             sum_tile(stages[1]);
+            rot(R0, t + 2);
             put(stages[0], R0);                      // tile t + 2
             wait_vm_lgkm0<63>();
             wg_barrier();
@@ -876,7 +959,12 @@ struct QSplit {
 //   complete during the following tile.
 // With one tile per block the next Q is loaded after the tile's scores and
 // the tile waits for every load.
-template <int D, int BLK, int NW, int TJ, int NST, int LA>
+//
+// With ROPE, q and k are rotated on the way in: each block's Q in registers
+// once its loads have landed, each K tile in LDS by the waves that loaded
+// column blocks 0 and 1 of its row groups, right after their own wait for
+// that tile (before the barrier that publishes it).
+template <int D, int BLK, int NW, int TJ, int NST, int LA, bool ROPE>
 __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     using T = bf16_t;
     using C = Cfg<T, D, BLK, NW>;
@@ -939,10 +1027,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     __amdgpu_buffer_rsrc_t drs[IPW];
 #pragma unroll
     for (int ii = 0; ii < IPW; ++ii) {
-        const int gi = w * IPW + ii;
-        const bool isv = gi >= NI;
-        const int x = isv ? gi - NI : gi;
-        const int blk = x / (TJ / 16), row0 = 16 * (x % (TJ / 16));
+        bool isv;
+        int blk, row0;
+        dma_piece<NI, IPW, TJ / 16, ROPE>(w * IPW + ii, isv, blk, row0);
         const int row = row0 + (l >> 2);
         dvo[ii] = (uint32_t)(row * RB + blk * 64 + (((l & 3) ^ LT::swz(row)) << 4));
         dlo[ii] = (isv ? TB : 0) + blk * LT::BLOCK + row0 * 64;
@@ -958,13 +1045,17 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     // elements 8g..8g+7 of each 32-element group kc
     uint32_t qvo[C::NSW], ovo[C::NSW];
     const bool odd = g & 1;
+    // O store m writes columns 16 (ct0 + 2m) + 4g .. +7 (even g) or
+    // 16 (ct0 + 2m + 1) + 4 (g - 1) .. +7 (odd g): 64 m bytes further on
+    auto o_off = [&](int si, int cc, int gg) {
+        const int r = 16 * slab_of<BLK, NW>(w, si) + cc;
+        return (uint32_t)(r * RB + 2 * ((gg & 1) ? 16 * (ct0 + 1) + 4 * (gg - 1) : 16 * ct0 + 4 * gg));
+    };
 #pragma unroll
     for (int si = 0; si < C::NSW; ++si) {
         const int r = 16 * slab_of<BLK, NW>(w, si) + c;
         qvo[si] = (uint32_t)(r * RB + g * 16);
-        // O store m writes columns 16 (ct0 + 2m) + 4g .. +7 (even g) or
-        // 16 (ct0 + 2m + 1) + 4 (g - 1) .. +7 (odd g): 64 m bytes further on
-        ovo[si] = (uint32_t)(r * RB + 2 * (odd ? 16 * (ct0 + 1) + 4 * (g - 1) : 16 * ct0 + 4 * g));
+        ovo[si] = o_off(si, c, g);
     }
     // Q of the current block, and of the next one (requested a tile early
     // when blocks have two or more tiles)
@@ -996,6 +1087,61 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
                            u32x2_t{pack_bf16x2(Sx[ia][ib][0], Sx[ia][ib][1]), pack_bf16x2(Sx[ia][ib][2], Sx[ia][ib][3])});
     };
 
+    // ---- rotary embedding: K rows of tile `tile` in its ring stage (by the
+    // lanes that loaded them), the Q rows of the block starting at token tq
+    [[maybe_unused]] const RopeK rk_lane = rope_k_lane<D, TJ>(w, l);
+    [[maybe_unused]] double rho = 0.0, rho8 = 0.0;
+    [[maybe_unused]] int64_t pbase = 0;
+    if constexpr (ROPE) {
+        rho = uniform_f64(rope_rho(p.rope_base, p.rope_dims));
+        rho8 = uniform_f64(rho * rho * rho * rho * rho * rho * rho * rho);
+        pbase = (p.pos0 ? (int64_t)p.pos0[s] : 0) + t0;
+    }
+    // (lane-derived values are taken from lane_id_fresh() so that the pair
+    // frequencies are recomputed at each use rather than held in registers)
+    auto rot_k = [&](char *stage, int tile) {
+        if constexpr (ROPE) {
+            if (rk_lane.on) {
+                const int lf = (int)lane_id_fresh();
+                const RopeK rf = rope_k_lane<D, TJ>(w, lf);
+                const double pos = (double)(pbase + (int64_t)tile * TJ + rf.rowk);
+                u32x4_t *a = reinterpret_cast<u32x4_t *>(stage + dlo[0] + 16 * lf);
+                if constexpr (D == 128) {
+                    // the lane's chunk of column block 0 and, a block further, its partner
+                    u32x4_t *b = reinterpret_cast<u32x4_t *>(stage + dlo[0] + LT::BLOCK + 16 * lf);
+                    u32x4_t x = *a, y = *b;
+                    rope_rot8(x, y, pos, rope_f(8 * rf.lc, rho8), rho);
+                    *a = x;
+                    *b = y;
+                } else {
+                    // partner: chunk lc ^ 2 of the same row, brought by lane l ^ 2
+                    const u32x4_t x = *a;
+                    const u32x4_t y = *reinterpret_cast<const u32x4_t *>(stage + dlo[0] + 16 * (lf ^ 2));
+                    *a = rope_rot8_half(x, y, rf.lc < 2, pos, rope_f(8 * (rf.lc & 1), rho8), rho);
+                }
+            }
+        }
+    };
+    auto rot_q = [&](Frag<T> (&Q)[C::NSW][C::KC], int tq) {
+        if constexpr (ROPE) {
+            const int lf = lane_id_fresh(), cf = lf & 15, gf = lf >> 4;
+#pragma unroll
+            for (int si = 0; si < C::NSW; ++si) {
+                const double pos = (double)(pbase + tq + 16 * slab_of<BLK, NW>(w, si) + cf);
+                if constexpr (D == 128) {
+                    // dims 8g .. 8g+7 (group 0) pair with dims 32 + 8g .. (group 1)
+                    rope_rot8(Q[si][0].u, Q[si][1].u, pos, rope_f(8 * gf, rho8), rho);
+                } else {
+                    // dims 8g .. 8g+7 of group 0 pair with lane l ^ 32's (g ^ 2)
+                    u32x4_t other;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) other[d] = (uint32_t)__shfl_xor((int)Q[si][0].u[d], 32);
+                    Q[si][0].u = rope_rot8_half(Q[si][0].u, other, gf < 2, pos, rope_f(8 * (gf & 1), rho8), rho);
+                }
+            }
+        }
+    };
+
     // ---- prologue: the first block's Q, tile 0 (and tile 1 when three are
     // kept in flight), the state at the chunk start (exclusive prefix from
     // the scan; zero for a sequence's first chunk); tile LA - 1 stays in flight
@@ -1016,7 +1162,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         write_state(S);
     }
     wait_vm_lgkm0<0>();
+    if constexpr (ROPE) {
+        rot_q(Q, 0);
+        rot_k(stages[0], 0);
+    }
     if constexpr (LA >= 2) issue(LA - 1, stages[LA - 1]);
+    if constexpr (ROPE) wait_vm_lgkm0<63>();         // the rotated tile is written
     wg_barrier();
 
     f32x4_t O[C::NSW][C::NCT];
@@ -1028,7 +1179,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     auto store_o = [&](int bi) {
 #pragma unroll
         for (int si = 0; si < C::NSW; ++si) {
-            const int vo = (int)ovo[si] + bi * BLK * RB;
+            // (with ROPE recomputed here, which keeps a register free)
+            const int lf = ROPE ? (int)lane_id_fresh() : 0;
+            const int vo = (int)(ROPE ? o_off(si, lf & 15, lf >> 4) : ovo[si]) + bi * BLK * RB;
 #pragma unroll
             for (int m = 0; m < C::NCT / 2; ++m) {
                 const uint32_t e0 = pack_bf16x2(O[si][2 * m][0], O[si][2 * m][1]);
@@ -1178,21 +1331,36 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
             // reloaded in this tile and everything is waited for)
             if constexpr (TPB == 1) {
                 wait_vm_lgkm0<0>();
+                if constexpr (ROPE) {
+                    if (jt == jl) store_o(bi);           // frees O before the rotations
+                    if (more) rot_q(Q, tb + BLK);
+                }
             } else {
                 wait_vm_lgkm0<(LA >= 2 ? (LA - 2) * IPW : 0)>();
+                if constexpr (ROPE) {
+                    if (jt == jl) store_o(bi);           // frees O before the rotations
+                    if (more) rot_q(Qn, tb + BLK);
+                }
 #pragma unroll
                 for (int si = 0; si < C::NSW; ++si)
 #pragma unroll
                     for (int kc = 0; kc < C::KC; ++kc) Q[si][kc] = Qn[si][kc];
             }
+            if constexpr (ROPE) rot_k(stages[(J + 1) % NST], t + 1);
             if constexpr (LA > 1) issue(t + LA, stages[(J + LA) % NST]);
+            if constexpr (ROPE) wait_vm_lgkm0<63>();     // the rotated tile is written
         } else {
             if (more || fdst) state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
             // DMA(t+1) has landed; younger are DMA(t+2 .. t+LA) and the Q
             // loads of the LA-1 tiles up to this one
             wait_vm_lgkm0<(LA - 1) * IPW + (LA >= 2 ? QS::n(jt) : 0) + (LA >= 3 ? QS::n(jt - 1) : 0)>();
+            if constexpr (ROPE) {
+                if (jt == jl) store_o(bi);               // frees O before the rotation
+                rot_k(stages[(J + 1) % NST], t + 1);
+                wait_vm_lgkm0<63>();                     // the rotated tile is written
+            }
         }
-        if (jt == jl) store_o(bi);
+        if (!ROPE && jt == jl) store_o(bi);
         wg_barrier();
     };
 
@@ -1215,7 +1383,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
 // Waves per workgroup of the bf16 fused kernel.
 constexpr int fused_waves(int D, int BLK) { return (D == 128 && BLK == 256) ? 16 : 8; }
 
-template <typename T, int D, int BLK>
+template <typename T, int D, int BLK, bool ROPE>
 static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream_t st, void *const *ev) {
     auto mark = [&](int i) {
         if (ev) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), st);
@@ -1229,7 +1397,7 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
     // the chunk summaries before it; with one chunk per sequence there is none.
     if (!plan.single_chunk) {
         if constexpr (sizeof(T) == 2)
-            hipLaunchKernelGGL((k_summary_reg<D, BLK, 8>), gchunks, dim3(512), 0, st, kp);
+            hipLaunchKernelGGL((k_summary_reg<D, BLK, 8, ROPE>), gchunks, dim3(512), 0, st, kp);
         else
             hipLaunchKernelGGL((k_summary<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
     }
@@ -1247,7 +1415,7 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
     if constexpr (sizeof(T) == 2)
         {
         constexpr int NWF = fused_waves(D, BLK);
-        hipLaunchKernelGGL((k_fused_dma<D, BLK, NWF, 64, 4, 2>), gchunks, dim3(NWF * 64), 0, st, kp);
+        hipLaunchKernelGGL((k_fused_dma<D, BLK, NWF, 64, 4, 2, ROPE>), gchunks, dim3(NWF * 64), 0, st, kp);
     }
     else
         hipLaunchKernelGGL((k_fused<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
@@ -1255,13 +1423,13 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
     return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool ROPE = false>
 static hipError_t launch_blk(const KParams &kp, const FwdPlan &plan, int blk, hipStream_t st,
                              void *const *ev) {
     switch (blk) {
-        case 64: return launch_typed<T, D, 64>(kp, plan, st, ev);
-        case 128: return launch_typed<T, D, 128>(kp, plan, st, ev);
-        default: return launch_typed<T, D, 256>(kp, plan, st, ev);
+        case 64: return launch_typed<T, D, 64, ROPE>(kp, plan, st, ev);
+        case 128: return launch_typed<T, D, 128, ROPE>(kp, plan, st, ev);
+        default: return launch_typed<T, D, 256, ROPE>(kp, plan, st, ev);
     }
 }
 
@@ -1298,9 +1466,16 @@ int launch_fwd(const FwdArgs &a, void *stream, void *const *events) {
     kp.s_init = a.s_init;
     kp.s_final = a.s_final;
     kp.init_mode = a.s_init == nullptr ? 0 : (a.plan.single_chunk ? 2 : 1);
+    kp.pos0 = a.pos0;
+    kp.rope_base = a.rope_base;
+    kp.rope_dims = a.rope_dims;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
-    if (a.dtype == 0) {
+    if (a.rope_dims > 0) {
+        // bf16 only, rope_dims == head_dim / 2 (checked by the caller)
+        e = a.head_dim == 64 ? launch_blk<bf16_t, 64, true>(kp, a.plan, a.block_size, st, events)
+                             : launch_blk<bf16_t, 128, true>(kp, a.plan, a.block_size, st, events);
+    } else if (a.dtype == 0) {
         e = a.head_dim == 64 ? launch_blk<bf16_t, 64>(kp, a.plan, a.block_size, st, events)
                              : launch_blk<bf16_t, 128>(kp, a.plan, a.block_size, st, events);
     } else {

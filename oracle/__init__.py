@@ -304,6 +304,27 @@ def causal_linear_attention_rope_varlen(q, k, v, cu_seqlens, rope_dims: int, bas
     return o, Sf
 
 
+def causal_linear_attention_rope_rows(q, k, v, rows, rope_dims: int, base: float, p0: int = 0,
+                                      S0=None) -> np.ndarray:
+    """Selected output rows of one [n, d] unit with q and k rotated at
+    positions p0 + t, straight from the definition:
+    o_t = (R q_t) S0 + sum_{j<=t} ((R q_t) . (R k_j)) v_j.  Cost O(n d) per row,
+    for spot checks of long sequences."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    n, d = q.shape
+    rows = np.asarray(rows, np.int64)
+    kr = rope(k, p0 + np.arange(n), rope_dims, base)
+    qr = rope(q[rows], p0 + rows, rope_dims, base)
+    out = np.zeros((len(rows), d))
+    for m, t in enumerate(rows):
+        out[m] = (kr[:t + 1] @ qr[m]) @ v[:t + 1]
+        if S0 is not None:
+            out[m] += qr[m] @ np.asarray(S0, np.float64)
+    return out
+
+
 def decode_rope(q, k, v, S0, positions, rope_dims: int, base: float):
     """Decode steps with rotated q and k: q, k, v [steps, units, d], S0 [units,
     d, d], positions [units] of the first step (step t is at positions + t).

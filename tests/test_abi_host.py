@@ -103,6 +103,35 @@ def test_decode_rejects(la):
     assert la.lightning_attn_decode(fake, fake, fake, None, fake, 1, 1, 64, 0, None) == 1
 
 
+def test_rope_rejects(la):
+    """Rotary arguments are checked on the host before any launch."""
+    fake = 1 << 20
+    need = la.lightning_attn_fwd_workspace_size(1, 1, 10, 128, 64, 0, 0)
+
+    def fr(d, dt, r, base):
+        return la.lightning_attn_fwd_rope(fake, fake, fake, fake, 1, 1, 10, d, 64, None, dt, r, base,
+                                          None, None, None, fake, need, None)
+    assert fr(128, 1, 64, 1e4) == 2          # fp32 input: unsupported with rotation
+    assert fr(128, 0, 32, 1e4) == 2          # only half the head dims
+    assert fr(128, 0, 128, 1e4) == 2
+    assert fr(128, 0, 0, 1e4) == 2           # the rotary entry point needs rope_dims > 0
+    assert fr(128, 0, 64, 0.0) == 1          # base must be positive and finite
+    assert fr(128, 0, 64, -2.0) == 1
+    assert fr(128, 0, 64, float("inf")) == 1
+    assert fr(128, 0, 64, float("nan")) == 1
+
+    def dr(d, dt, r, base, pos=fake, state=fake, slots=None, nslots=0):
+        return la.lightning_attn_decode_rope(fake, fake, fake, state, nslots, slots, fake, 1, 1, d, dt,
+                                             r, base, pos, None)
+    assert dr(128, 0, 32, 1e4) == 2
+    assert dr(64, 0, 64, 1e4) == 2
+    assert dr(128, 0, 64, 0.0) == 1
+    assert dr(128, 0, 64, 1e4, pos=None) == 1      # positions are required
+    assert dr(128, 0, 64, 1e4, state=None) == 1    # dense states are required
+    assert dr(128, 0, 64, 1e4, state=None, slots=fake, nslots=2) == 1
+    assert dr(128, 5, 64, 1e4) == 2
+
+
 def test_product_never_imports_oracle():
     """The HIP path must not route through the CPU oracle."""
     pkg = os.path.join(ROOT, "linear_attention_attn_amd")

@@ -188,6 +188,19 @@ def test_rope_attention(O):
         pins.check_rope_resume(ratt(O, r, base))
 
 
+def test_rope_rows_match_full_form(O):
+    """The row-wise spot-check form equals the full closed form."""
+    rng = np.random.default_rng(63)
+    n, d, r, base = 50, 8, 4, 1e7
+    q, k, v = (rng.standard_normal((n, d)).astype(np.float32) for _ in range(3))
+    S0 = rng.standard_normal((d, d))
+    o, _ = O.causal_linear_attention_rope(q[None, None], k[None, None], v[None, None], r, base,
+                                          [777], S0[None, None])
+    rows = [0, 1, 17, 49]
+    orow = O.causal_linear_attention_rope_rows(q, k, v, rows, r, base, 777, S0)
+    assert np.allclose(orow, o[0, 0, rows], rtol=0, atol=1e-12 * np.abs(o).max())
+
+
 def test_rope_attention_varlen_and_decode(O):
     """Packed sequences restart their positions (plus their offset) at each
     sequence's first token; decode at positions continuing a prefill matches
