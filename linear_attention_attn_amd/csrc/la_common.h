@@ -281,19 +281,47 @@ __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 // rho = base^(-2/r), the ratio f_{i+1} / f_i.
 __device__ __forceinline__ double rope_rho(double base, int r) { return exp2(-2.0 / r * log2(base)); }
 
-// f_{i0} = rho^{i0} / (2 pi) for i0 a multiple of 8 below 64, from rho8 = rho^8.
-__device__ __forceinline__ double rope_f(int i0, double rho8) {
-    double f = 0.5 / 3.14159265358979323846;
-#pragma unroll
-    for (int j = 1; j < 8; ++j)
-        if (8 * j <= i0) f *= rho8;
-    return f;
+// A kernel-uniform double held in scalar registers.
+__device__ __forceinline__ double uniform_f64(double x) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Frequencies in turns of the first pair of each group of eight:
+// fj = f_{8j} = rho^{8j} / (2 pi), j < 4 (kernel-uniform, scalar registers;
+// separate members, not an array, so that a lane's pick is a register select).
+struct RopeFreqs {
+    double f0, f1, f2, f3;
+    double rho;
+};
+
+__device__ __forceinline__ RopeFreqs rope_freqs(double base, int r) {
+    RopeFreqs q;
+    q.rho = uniform_f64(rope_rho(base, r));
+    const double r8 = q.rho * q.rho * q.rho * q.rho * q.rho * q.rho * q.rho * q.rho;
+    const double f0 = 0.5 / 3.14159265358979323846;
+    q.f0 = uniform_f64(f0);
+    q.f1 = uniform_f64(f0 * r8);
+    q.f2 = uniform_f64(f0 * r8 * r8);
+    q.f3 = uniform_f64(f0 * r8 * r8 * r8);
+    return q;
+}
+
+// f_{8 grp} for a lane's pair group grp (0..3), picked with bit masks (a
+// plain select of the members can be turned into an indexed load from a
+// stack copy of the struct).
+__device__ __forceinline__ double rope_f(int grp, const RopeFreqs &q) {
+    const uint64_t m1 = 0ull - (uint64_t)(grp & 1), m2 = 0ull - (uint64_t)((grp >> 1) & 1);
+    const uint64_t f0 = __builtin_bit_cast(uint64_t, q.f0), f1 = __builtin_bit_cast(uint64_t, q.f1);
+    const uint64_t f2 = __builtin_bit_cast(uint64_t, q.f2), f3 = __builtin_bit_cast(uint64_t, q.f3);
+    const uint64_t lo = (f0 & ~m1) | (f1 & m1), hi = (f2 & ~m1) | (f3 & m1);
+    return __builtin_bit_cast(double, (lo & ~m2) | (hi & m2));
 }
 
 __device__ __forceinline__ void rope_cs(double pos, double f, float &c, float &s) {
-    double t = pos * f;
-    t -= floor(t);
-    const float tf = (float)t;
+    const float tf = (float)__builtin_amdgcn_fract(pos * f);   // in [0, 1)
     s = __builtin_amdgcn_sinf(tf);
     c = __builtin_amdgcn_cosf(tf);
 }

@@ -756,14 +756,6 @@ __device__ __forceinline__ RopeK rope_k_lane(int w, int l) {
     return r;
 }
 
-// A kernel-uniform double held in scalar registers.
-__device__ __forceinline__ double uniform_f64(double x) {
-    const uint64_t b = __builtin_bit_cast(uint64_t, x);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-
 // U_c = K_c^T V_c over a chunk, with the K/V tiles staged through
 // registers: each wave loads its 16-byte pieces of tile t + 2 into registers
 // (buffer loads, rows past the chunk end read as zeros) while tile t is
@@ -827,11 +819,10 @@ __global__ __launch_bounds__(NW * 64, 1024 / (NW * 64)) void k_summary_reg(KPara
     u32x4_t R0[IPW], R1[IPW];
     // rotary embedding of the K rows this lane brings (tile `tile`)
     [[maybe_unused]] const RopeK rk_lane = rope_k_lane<D, TJ>(w, l);
-    [[maybe_unused]] double rho = 0.0, rho8 = 0.0;
+    [[maybe_unused]] RopeFreqs rf8{};
     [[maybe_unused]] int64_t pbase = 0;
     if constexpr (ROPE) {
-        rho = uniform_f64(rope_rho(p.rope_base, p.rope_dims));
-        rho8 = uniform_f64(rho * rho * rho * rho * rho * rho * rho * rho);
+        rf8 = rope_freqs(p.rope_base, p.rope_dims);
         pbase = (p.pos0 ? (int64_t)p.pos0[s] : 0) + t0;
     }
     auto rot = [&](u32x4_t (&R)[IPW], int tile) {
@@ -839,13 +830,13 @@ __global__ __launch_bounds__(NW * 64, 1024 / (NW * 64)) void k_summary_reg(KPara
             if (rk_lane.on) {
                 const double pos = (double)(pbase + (int64_t)tile * TJ + rk_lane.rowk);
                 if constexpr (D == 128) {
-                    rope_rot8(R[0], R[1], pos, rope_f(8 * rk_lane.lc, rho8), rho);
+                    rope_rot8(R[0], R[1], pos, rope_f(rk_lane.lc, rf8), rf8.rho);
                 } else {
                     u32x4_t other;
 #pragma unroll
                     for (int d = 0; d < 4; ++d)   // lane l ^ 2 holds chunk lc ^ 2 of the same row
                         other[d] = (uint32_t)__builtin_amdgcn_mov_dpp((int)R[0][d], 0x4E, 0xF, 0xF, false);
-                    R[0] = rope_rot8_half(R[0], other, rk_lane.lc < 2, pos, rope_f(8 * (rk_lane.lc & 1), rho8), rho);
+                    R[0] = rope_rot8_half(R[0], other, rk_lane.lc < 2, pos, rope_f(rk_lane.lc & 1, rf8), rf8.rho);
                 }
             }
         }
@@ -1090,11 +1081,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     // ---- rotary embedding: K rows of tile `tile` in its ring stage (by the
     // lanes that loaded them), the Q rows of the block starting at token tq
     [[maybe_unused]] const RopeK rk_lane = rope_k_lane<D, TJ>(w, l);
-    [[maybe_unused]] double rho = 0.0, rho8 = 0.0;
+    [[maybe_unused]] RopeFreqs rf8{};
     [[maybe_unused]] int64_t pbase = 0;
     if constexpr (ROPE) {
-        rho = uniform_f64(rope_rho(p.rope_base, p.rope_dims));
-        rho8 = uniform_f64(rho * rho * rho * rho * rho * rho * rho * rho);
+        rf8 = rope_freqs(p.rope_base, p.rope_dims);
         pbase = (p.pos0 ? (int64_t)p.pos0[s] : 0) + t0;
     }
     // (lane-derived values are taken from lane_id_fresh() so that the pair
@@ -1110,14 +1100,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
                     // the lane's chunk of column block 0 and, a block further, its partner
                     u32x4_t *b = reinterpret_cast<u32x4_t *>(stage + dlo[0] + LT::BLOCK + 16 * lf);
                     u32x4_t x = *a, y = *b;
-                    rope_rot8(x, y, pos, rope_f(8 * rf.lc, rho8), rho);
+                    rope_rot8(x, y, pos, rope_f(rf.lc, rf8), rf8.rho);
                     *a = x;
                     *b = y;
                 } else {
                     // partner: chunk lc ^ 2 of the same row, brought by lane l ^ 2
                     const u32x4_t x = *a;
                     const u32x4_t y = *reinterpret_cast<const u32x4_t *>(stage + dlo[0] + 16 * (lf ^ 2));
-                    *a = rope_rot8_half(x, y, rf.lc < 2, pos, rope_f(8 * (rf.lc & 1), rho8), rho);
+                    *a = rope_rot8_half(x, y, rf.lc < 2, pos, rope_f(rf.lc & 1, rf8), rf8.rho);
                 }
             }
         }
@@ -1130,13 +1120,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
                 const double pos = (double)(pbase + tq + 16 * slab_of<BLK, NW>(w, si) + cf);
                 if constexpr (D == 128) {
                     // dims 8g .. 8g+7 (group 0) pair with dims 32 + 8g .. (group 1)
-                    rope_rot8(Q[si][0].u, Q[si][1].u, pos, rope_f(8 * gf, rho8), rho);
+                    rope_rot8(Q[si][0].u, Q[si][1].u, pos, rope_f(gf, rf8), rf8.rho);
                 } else {
                     // dims 8g .. 8g+7 of group 0 pair with lane l ^ 32's (g ^ 2)
                     u32x4_t other;
 #pragma unroll
                     for (int d = 0; d < 4; ++d) other[d] = (uint32_t)__shfl_xor((int)Q[si][0].u[d], 32);
-                    Q[si][0].u = rope_rot8_half(Q[si][0].u, other, gf < 2, pos, rope_f(8 * (gf & 1), rho8), rho);
+                    Q[si][0].u = rope_rot8_half(Q[si][0].u, other, gf < 2, pos, rope_f(gf & 1, rf8), rf8.rho);
                 }
             }
         }
@@ -1235,6 +1225,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
                 sched_fence();
             }
         }
+        if constexpr (ROPE && last && TPB > 1) {
+            // the rotated dims of the next block's Q were requested in the
+            // block's earlier tiles: rotate them while this tile's products run
+            if (more) rot_q(Qn, tb + BLK);
+        }
 
         // ---- intra-block left product for this K/V tile
 #pragma unroll
@@ -1309,6 +1304,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
             }
         }
 
+        // rotate the next tile's keys (its DMA was requested a tile ago) while
+        // the other waves are still on this tile's products; the barrier at
+        // the end of the tile publishes them
+        if constexpr (ROPE) rot_k(stages[(J + 1) % NST], t + 1);
+
         const char *ka[C::SA];
         const char *vbs[C::SB];
 #pragma unroll
@@ -1332,35 +1332,23 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
             if constexpr (TPB == 1) {
                 wait_vm_lgkm0<0>();
                 if constexpr (ROPE) {
-                    if (jt == jl) store_o(bi);           // frees O before the rotations
-                    if (more) rot_q(Q, tb + BLK);
+                    if (more) rot_q(Q, tb + BLK);        // loaded in this tile
                 }
             } else {
                 wait_vm_lgkm0<(LA >= 2 ? (LA - 2) * IPW : 0)>();
-                if constexpr (ROPE) {
-                    if (jt == jl) store_o(bi);           // frees O before the rotations
-                    if (more) rot_q(Qn, tb + BLK);
-                }
 #pragma unroll
                 for (int si = 0; si < C::NSW; ++si)
 #pragma unroll
                     for (int kc = 0; kc < C::KC; ++kc) Q[si][kc] = Qn[si][kc];
             }
-            if constexpr (ROPE) rot_k(stages[(J + 1) % NST], t + 1);
             if constexpr (LA > 1) issue(t + LA, stages[(J + LA) % NST]);
-            if constexpr (ROPE) wait_vm_lgkm0<63>();     // the rotated tile is written
         } else {
             if (more || fdst) state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
             // DMA(t+1) has landed; younger are DMA(t+2 .. t+LA) and the Q
             // loads of the LA-1 tiles up to this one
             wait_vm_lgkm0<(LA - 1) * IPW + (LA >= 2 ? QS::n(jt) : 0) + (LA >= 3 ? QS::n(jt - 1) : 0)>();
-            if constexpr (ROPE) {
-                if (jt == jl) store_o(bi);               // frees O before the rotation
-                rot_k(stages[(J + 1) % NST], t + 1);
-                wait_vm_lgkm0<63>();                     // the rotated tile is written
-            }
         }
-        if (!ROPE && jt == jl) store_o(bi);
+        if (jt == jl) store_o(bi);
         wg_barrier();
     };
 
