@@ -38,60 +38,105 @@ static int64_t env_i64(const char *name, int64_t dflt) {
 }
 
 // Chunk length C (tokens one workgroup walks carrying the state; a multiple
-// of the block size).  The work is W = units * average length head-tokens
-// over kCUs compute units.  When W / kCUs covers a whole sequence, every
-// sequence is one chunk: no chunk summary or scan is needed at all.
-// Otherwise C is the largest power of two <= W / kCUs (so there are at least
-// about kCUs chunks), at most kMaxChunk: the per-chunk state traffic (a d x d
-// fp32 state written, scanned and read once per chunk) is then a few percent
-// of the 4 * d * 2 bytes per token of q, k, v and o.  LA_CHUNK_TOKENS
-// overrides it (rounded down to a multiple of the block size).
+// of the block size) and sub-chunk length C_s (the K^T V summary granularity;
+// C is a multiple of C_s, C_s <= kSub).
+//
+// Dense input: every candidate C is priced with a simple model of the two
+// passes in units of "tokens one CU streams through the fused kernel":
+//   fused   = ceil(units * n / kCUs) * C      (rounds of one chunk per CU)
+//   summary = kSum * units * (n - 1) * C / kCUs   (every chunk but the last is
+//             summarised; measured ~0.45 of the fused cost per token)
+//   scan    = kScan * units * n_s / kCUs      (three passes over 64 KiB fp32
+//             states per sub-chunk, ~190 token-equivalents each)
+// with n = ceil(L / C) chunks and n_s = ceil(L / C_s) sub-chunks per unit.
+// Candidates: one chunk per sequence (no summary or scan at all), powers of
+// two from the block size to kSub, and multiples of kSub (sub-chunks of kSub),
+// all within the 32-bit buffer offsets of the bf16 kernels (2^30 bytes of a
+// chunk's rows).  E.g. 64 heads x 1M tokens: C = 262144 (4 chunks per head,
+// one workgroup per CU) with sub-chunks of 16384, so the summaries read 3/4
+// of k and v instead of 63/64 with 16384-token chunks.
+//
+// Packed input: C = C_s = the largest power of two <= W / kCUs (W = all
+// head-tokens), at most kSub, so there are at least about kCUs chunks and a
+// long sequence does not hold one CU for much longer than the others.
+//
+// LA_CHUNK_TOKENS forces C (a multiple of the block size, and of kSub above
+// it); LA_SUB_TOKENS forces C_s (a multiple of the block size dividing C).
 void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int block_size, bool varlen,
                    FwdPlan *plan) {
     const int64_t kCUs = env_i64("LA_TARGET_GROUPS", 256);
-    const int64_t kMaxChunk = 16384;
+    const int64_t kSub = 16384;
+    const double kSum = 0.45, kScan = 190.0;
     const int64_t units = (int64_t)batch * heads;
-    const int64_t lavg = std::max<int64_t>(1, varlen ? seq_len / batch : seq_len);
-    const int64_t per_cu = std::max<int64_t>(1, units * lavg / kCUs);
+    const int64_t B = block_size;
+    const int64_t cap = (((int64_t)1 << 30) / (head_dim * 2)) / B * B;
+    auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
+
     int64_t C;
-    // One chunk per sequence while the chunk's rows stay within the 32-bit
-    // buffer offsets of the bf16 kernels (2^30 bytes, with margin).
-    const bool fits = seq_len * (int64_t)head_dim * 2 <= ((int64_t)1 << 30);
-    if (!varlen && per_cu >= seq_len && fits) {
-        C = (seq_len + block_size - 1) / block_size * block_size;   // one chunk per sequence
+    if (!varlen) {
+        const int64_t L = std::max<int64_t>(1, seq_len);
+        auto cost = [&](int64_t c) {
+            const int64_t n = cdiv(L, c);
+            const int64_t cs = n == 1 ? c : std::min(c, kSub);
+            const double fused = (double)cdiv(units * n, kCUs) * (double)std::min(c, L);
+            const double summ = kSum * (double)units * (double)(n - 1) * (double)c / (double)kCUs;
+            const double scan = n == 1 ? 0.0 : kScan * (double)units * (double)cdiv(L, cs) / (double)kCUs;
+            return fused + summ + scan;
+        };
+        C = B;
+        double best = cost(C);
+        auto consider = [&](int64_t c) {
+            if (c < B || c > cap || c % B) return;
+            const double v = cost(c);
+            if (v < best) { best = v; C = c; }       // ties keep the smaller chunk
+        };
+        for (int64_t c = B; c <= kSub; c *= 2) consider(c);
+        for (int64_t m = 2; m * kSub < L + kSub && m * kSub <= cap; ++m) consider(m * kSub);
+        consider(cdiv(L, B) * B);                     // one chunk per sequence
     } else {
-        C = block_size;
-        while (C * 2 <= kMaxChunk && C * 2 <= per_cu) C *= 2;
+        const int64_t lavg = std::max<int64_t>(1, seq_len / batch);
+        const int64_t per_cu = std::max<int64_t>(1, units * lavg / kCUs);
+        C = B;
+        while (C * 2 <= kSub && C * 2 <= per_cu) C *= 2;
     }
     const int64_t forced = env_i64("LA_CHUNK_TOKENS", 0);
     if (forced > 0) {
-        const int64_t cap = (((int64_t)1 << 30) / (head_dim * 2)) / block_size * block_size;
-        C = std::max<int64_t>(block_size, std::min(cap, forced / block_size * block_size));
+        C = std::max<int64_t>(B, std::min(cap, forced / B * B));
+        if (C > kSub) C = C / kSub * kSub;
     }
+    const bool one = !varlen && cdiv(std::max<int64_t>(1, seq_len), C) == 1;
+    int64_t Cs = one ? C : std::min(C, kSub);
+    const int64_t fs = env_i64("LA_SUB_TOKENS", 0);
+    if (fs > 0 && !one && fs % B == 0 && fs <= C && C % fs == 0) Cs = fs;
 
     const int G = 32;
     FwdPlan p;
     p.chunk = C;
+    p.sub = Cs;
     p.scan_group = G;
     if (!varlen) {
-        const int64_t cps = (seq_len + C - 1) / C;
+        const int64_t cps = cdiv(seq_len, C), sps = cdiv(seq_len, Cs);
         p.nchunk_ub = (int64_t)batch * cps;
-        p.ntile_ub = (int64_t)batch * ((cps + G - 1) / G);
-        p.scan_tiles = cps > G;
+        p.nsub_ub = (int64_t)batch * sps;
+        p.ntile_ub = (int64_t)batch * cdiv(sps, G);
+        p.scan_tiles = sps > G;
         p.single_chunk = cps == 1;
     } else {
         p.nchunk_ub = seq_len / C + batch;
-        p.ntile_ub = (p.nchunk_ub + G - 1) / G + batch;
-        p.scan_tiles = (seq_len + C - 1) / C > G;
+        p.nsub_ub = seq_len / Cs + batch;
+        p.ntile_ub = (p.nsub_ub + G - 1) / G + batch;
+        p.scan_tiles = cdiv(seq_len, Cs) > G;
     }
     const size_t dd = (size_t)head_dim * head_dim * sizeof(float);
     size_t off = 0;
     p.off_chunk_off = off;
     off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));
+    p.off_sub_off = off;
+    off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));
     p.off_tile_off = off;
     off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));
     p.off_states = off;
-    off = align256(off + (size_t)heads * (size_t)p.nchunk_ub * dd);
+    off = align256(off + (size_t)heads * (size_t)p.nsub_ub * dd);
     p.off_tilesum = off;
     if (p.scan_tiles) off = align256(off + (size_t)heads * (size_t)p.ntile_ub * dd);
     p.bytes = off;

@@ -9,18 +9,23 @@ namespace la {
 
 // How a forward pass is laid out.  A "chunk" is a run of C tokens of one
 // sequence (C a multiple of the block size) that one workgroup walks block by
-// block, carrying the d x d state; chunk states are joined by a parallel
-// segmented exclusive scan.
+// block, carrying the d x d state.  The state at each chunk's start comes
+// from a parallel segmented exclusive scan over the K^T V summaries of
+// "sub-chunks" of C_s tokens (C a multiple of C_s): chunks are sized to fill
+// the chip, sub-chunks to give the summary kernel enough workgroups.
 struct FwdPlan {
     int64_t chunk = 0;        // C, tokens per chunk
-    int scan_group = 0;       // G, chunks per scan tile
+    int64_t sub = 0;          // C_s, tokens per sub-chunk
+    int scan_group = 0;       // G, sub-chunks per scan tile
     int64_t nchunk_ub = 0;    // chunk slots per head (exact for dense input)
+    int64_t nsub_ub = 0;      // sub-chunk slots per head
     int64_t ntile_ub = 0;     // scan-tile slots per head
-    bool scan_tiles = false;  // some sequence may span more than G chunks
+    bool scan_tiles = false;  // some sequence may span more than G sub-chunks
     bool single_chunk = false;  // every sequence is one chunk: no summaries, no scan
     size_t off_chunk_off = 0; // int32 [nseq + 1]
+    size_t off_sub_off = 0;   // int32 [nseq + 1]
     size_t off_tile_off = 0;  // int32 [nseq + 1]
-    size_t off_states = 0;    // fp32 [heads][nchunk_ub][d][d]
+    size_t off_states = 0;    // fp32 [heads][nsub_ub][d][d]
     size_t off_tilesum = 0;   // fp32 [heads][ntile_ub][d][d]
     size_t bytes = 0;         // total workspace bytes
 };

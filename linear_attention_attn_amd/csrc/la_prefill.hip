@@ -8,15 +8,21 @@
 //     O_b = O_b^intra + Q_b S_b ,   S_b = sum over earlier blocks of K^T V .
 //
 // Kernels (all on the caller's stream, no host synchronisation):
-//   1. k_prep       chunk / scan-tile offset tables from cu_seqlens (1 WG)
-//   2. k_summary    U_c = K_c^T V_c for every chunk c of C tokens (MFMA)
-//   3. k_scan_*     fp32 exclusive prefix over chunk states, segmented at
+//   1. k_prep       chunk, sub-chunk and scan-tile offset tables from
+//                   cu_seqlens (1 WG)
+//   2. k_summary    U_c = K_c^T V_c for every sub-chunk c of C_s tokens that
+//                   precedes a sequence's last chunk (MFMA)
+//   3. k_scan_*     fp32 exclusive prefix over sub-chunk states, segmented at
 //                   sequence starts, as a three-phase reduce-then-scan across
-//                   chunk tiles (parallel over tiles and over the d*d lanes)
-//   4. k_fused      per chunk: start from its prefix state and walk the
-//                   chunk's blocks; per block the masked Q K^T and P V
-//                   products (MFMA, tiles staged in LDS) plus Q S, one store
-//                   of O, then S += K_b^T V_b for the next block.
+//                   tiles of sub-chunks (parallel over tiles and the d*d lanes)
+//   4. k_fused      per chunk of C tokens (C a multiple of C_s): start from
+//                   the prefix at its first sub-chunk and walk the chunk's
+//                   blocks; per block the masked Q K^T and P V products (MFMA,
+//                   tiles staged in LDS) plus Q S, one store of O, then
+//                   S += K_b^T V_b for the next block.
+// Chunks (one workgroup each) are sized to fill the chip; the summaries work
+// on sub-chunks of at most 16384 tokens so that they have enough workgroups of
+// their own, and skip the sequence's last chunk, whose prefix-sum is never needed.
 // The intra-block product and the output combine are one kernel: both
 // accumulate into the same registers (O^T = V^T P^T + S^T Q^T), so the
 // intra-block partial never goes to memory.
@@ -31,13 +37,15 @@ struct KParams {
     const void *q, *k, *v;
     void *o;
     const int32_t *cu;      // packed offsets, or nullptr (dense)
-    int32_t *chunk_off;     // [nseq + 1]
-    int32_t *tile_off;      // [nseq + 1]
-    float *states;          // [heads][nchunk_ub][D*D]
+    int32_t *chunk_off;     // [nseq + 1] chunks before each sequence
+    int32_t *sub_off;       // [nseq + 1] sub-chunks before each sequence
+    int32_t *tile_off;      // [nseq + 1] scan tiles before each sequence
+    float *states;          // [heads][nsub_ub][D*D]
     float *tilesum;         // [heads][ntile_ub][D*D]
     int64_t seq_len;        // dense: per sequence; packed: total tokens
-    int64_t chunk;          // tokens per chunk
-    int64_t nchunk_ub, ntile_ub;
+    int64_t chunk;          // tokens per chunk (a multiple of sub)
+    int64_t sub;            // tokens per sub-chunk
+    int64_t nchunk_ub, nsub_ub, ntile_ub;
     int nseq, heads, group;
     // state handoff: initial states [nseq][heads][D][D] (or nullptr = zero)
     // and final states of the same layout (or nullptr = not wanted).
@@ -85,16 +93,24 @@ __device__ __forceinline__ int find_seg(const int32_t *off, int n, int64_t x) {
     return lo;
 }
 
-// Source of the state at the start of chunk gch (chunk-local index cl) of
-// sequence s, head h, or nullptr for zero: the scanned prefix in `states`
-// (which includes a carried-in initial state when one was given), or with
-// one chunk per sequence the initial state itself.
+// Source of the state at the start of chunk cl (chunk-local index) of
+// sequence s, head h, or nullptr for zero: the scanned prefix in `states` at
+// the chunk's first sub-chunk (which includes a carried-in initial state when
+// one was given), or with one chunk per sequence the initial state itself.
 template <int D>
-__device__ __forceinline__ const float *chunk_start_state(const KParams &p, int s, int h, int64_t gch,
-                                                          int64_t cl) {
+__device__ __forceinline__ const float *chunk_start_state(const KParams &p, int s, int h, int64_t cl) {
     if (p.init_mode == 2) return p.s_init + ((int64_t)s * p.heads + h) * (D * D);
     if (p.init_mode == 0 && cl == 0) return nullptr;
-    return p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
+    const int64_t gsub = p.sub_off[s] + cl * (p.chunk / p.sub);
+    return p.states + ((int64_t)h * p.nsub_ub + gsub) * (D * D);
+}
+
+// Sub-chunk gsub of sequence s, or -1 when its summary is not needed (it lies
+// in the sequence's last chunk): its first token otherwise.
+__device__ __forceinline__ int64_t sub_first_token(const KParams &p, int s, int64_t gsub) {
+    const int64_t t0 = (gsub - p.sub_off[s]) * p.sub;
+    const int64_t nc = p.chunk_off[s + 1] - p.chunk_off[s];
+    return t0 >= (nc - 1) * p.chunk ? -1 : t0;
 }
 
 // Final state of (s, h) when the caller asked for it and chunk gch is the
@@ -117,41 +133,49 @@ __global__ __launch_bounds__(256) void k_state_empty(KParams p) {
 }
 
 // -------------------------------------------------------------- k_prep
-// chunk_off[s] = sum_{s' < s} ceil(L_s' / C);  tile_off[s] = sum ceil(nc_s' / G).
+// chunk_off[s] = sum_{s' < s} ceil(L_s' / C), sub_off[s] = sum ceil(L_s' / C_s),
+// tile_off[s] = sum ceil(ns_s' / G) (ns = sub-chunks of a sequence).
 constexpr int kPrepThreads = 1024;
 
 __global__ __launch_bounds__(kPrepThreads) void k_prep(KParams p) {
-    __shared__ int64_t sc[kPrepThreads], st[kPrepThreads];
+    __shared__ int64_t sc[kPrepThreads], su[kPrepThreads], st[kPrepThreads];
     const int t = threadIdx.x;
     const int per = (p.nseq + kPrepThreads - 1) / kPrepThreads;
     const int s0 = t * per, s1 = min(p.nseq, s0 + per);
-    int64_t c = 0, g = 0;
+    auto counts = [&](int s, int64_t &nc, int64_t &ns, int64_t &ng) {
+        const int64_t L = p.cu ? (int64_t)p.cu[s + 1] - p.cu[s] : p.seq_len;
+        nc = (L + p.chunk - 1) / p.chunk;
+        ns = (L + p.sub - 1) / p.sub;
+        ng = (ns + p.group - 1) / p.group;
+    };
+    int64_t c = 0, u = 0, g = 0;
     for (int s = s0; s < s1; ++s) {
-        int64_t L = p.cu ? (int64_t)p.cu[s + 1] - p.cu[s] : p.seq_len;
-        int64_t nc = (L + p.chunk - 1) / p.chunk;
-        c += nc;
-        g += (nc + p.group - 1) / p.group;
+        int64_t nc, ns, ng;
+        counts(s, nc, ns, ng);
+        c += nc; u += ns; g += ng;
     }
-    sc[t] = c; st[t] = g;
+    sc[t] = c; su[t] = u; st[t] = g;
     __syncthreads();
     for (int d = 1; d < kPrepThreads; d <<= 1) {   // inclusive Hillis-Steele scan
-        int64_t a = t >= d ? sc[t - d] : 0, b = t >= d ? st[t - d] : 0;
+        const int64_t a = t >= d ? sc[t - d] : 0, b = t >= d ? su[t - d] : 0, e = t >= d ? st[t - d] : 0;
         __syncthreads();
-        sc[t] += a; st[t] += b;
+        sc[t] += a; su[t] += b; st[t] += e;
         __syncthreads();
     }
     c = t ? sc[t - 1] : 0;
+    u = t ? su[t - 1] : 0;
     g = t ? st[t - 1] : 0;
     for (int s = s0; s < s1; ++s) {
         p.chunk_off[s] = (int32_t)c;
+        p.sub_off[s] = (int32_t)u;
         p.tile_off[s] = (int32_t)g;
-        int64_t L = p.cu ? (int64_t)p.cu[s + 1] - p.cu[s] : p.seq_len;
-        int64_t nc = (L + p.chunk - 1) / p.chunk;
-        c += nc;
-        g += (nc + p.group - 1) / p.group;
+        int64_t nc, ns, ng;
+        counts(s, nc, ns, ng);
+        c += nc; u += ns; g += ng;
     }
     if (t == kPrepThreads - 1) {
         p.chunk_off[p.nseq] = (int32_t)sc[t];
+        p.sub_off[p.nseq] = (int32_t)su[t];
         p.tile_off[p.nseq] = (int32_t)st[t];
     }
 }
@@ -302,20 +326,19 @@ __device__ __forceinline__ void state_update(f32x4_t (&S)[SA][SB], const char *k
 }
 
 // --------------------------------------------------------- k_summary
-// states[h][chunk] = K_c^T V_c  (fp32, row a = key dim, column b = value dim)
+// states[h][sub-chunk] = K_c^T V_c  (fp32, row a = key dim, column b = value dim)
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(512, 2) void k_summary(KParams p) {
     using C = Cfg<T, D, BLK>;
     __shared__ __attribute__((aligned(16))) char lds[2][2 * C::KT_BYTES];
     const int h = blockIdx.y;
     const int64_t gch = blockIdx.x;
-    if (gch >= p.chunk_off[p.nseq]) return;
-    const int s = find_seg(p.chunk_off, p.nseq, gch);
-    // The exclusive prefix never uses the last chunk of a sequence.
-    if (gch + 1 == p.chunk_off[s + 1]) return;
+    if (gch >= p.sub_off[p.nseq]) return;
+    const int s = find_seg(p.sub_off, p.nseq, gch);
+    const int64_t t0 = sub_first_token(p, s, gch);
+    if (t0 < 0) return;                              // in the sequence's last chunk: not needed
     const Unit u = unit_of<D>(p, s, h);
-    const int64_t t0 = (gch - p.chunk_off[s]) * p.chunk;
-    const int64_t t1 = min(u.len, t0 + p.chunk);
+    const int64_t t1 = min(u.len, t0 + p.sub);
     const T *kb = reinterpret_cast<const T *>(p.k) + u.base;
     const T *vb = reinterpret_cast<const T *>(p.v) + u.base;
 
@@ -340,7 +363,7 @@ __global__ __launch_bounds__(512, 2) void k_summary(KParams p) {
             patch_store<T, D, BLK, false>(pt, nullptr, lds[buf ^ 1], lds[buf ^ 1] + C::KT_BYTES);
         __syncthreads();
     }
-    float *dst = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
+    float *dst = p.states + ((int64_t)h * p.nsub_ub + gch) * (D * D);
 #pragma unroll
     for (int ia = 0; ia < C::SA; ++ia)
 #pragma unroll
@@ -351,11 +374,12 @@ __global__ __launch_bounds__(512, 2) void k_summary(KParams p) {
 }
 
 // ------------------------------------------------------------- scans
-// Exclusive prefix over the chunks of every (sequence, head), in place on
-// `states`.  Lanes are the d*d state entries; chunk tiles of G chunks are
+// Exclusive prefix over the sub-chunks of every (sequence, head), in place
+// on `states`.  Lanes are the d*d state entries; tiles of G sub-chunks are
 // reduced (A), the tile totals scanned per sequence (B), and each tile
 // rescanned from its prefix (C).  With every sequence inside one tile only
-// phase C runs.
+// phase C runs.  (Entries of sub-chunks in a sequence's last chunk hold no
+// summary; they only reach prefixes that are never read.)
 constexpr int kScanThreads = 256;
 
 template <int D>
@@ -364,10 +388,10 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(KParams p) {
     const int64_t tile = blockIdx.x;
     if (tile >= p.tile_off[p.nseq]) return;
     const int s = find_seg(p.tile_off, p.nseq, tile);
-    const int64_t c0 = p.chunk_off[s] + (tile - p.tile_off[s]) * p.group;
-    const int64_t c1 = min((int64_t)p.chunk_off[s + 1], c0 + p.group);
+    const int64_t c0 = p.sub_off[s] + (tile - p.tile_off[s]) * p.group;
+    const int64_t c1 = min((int64_t)p.sub_off[s + 1], c0 + p.group);
     const int e = blockIdx.y * kScanThreads + threadIdx.x;
-    const float *src = p.states + (int64_t)h * p.nchunk_ub * (D * D) + e;
+    const float *src = p.states + (int64_t)h * p.nsub_ub * (D * D) + e;
     float acc = 0.f;
     for (int64_t c = c0; c < c1; ++c) acc += src[c * (D * D)];
     p.tilesum[((int64_t)h * p.ntile_ub + tile) * (D * D) + e] = acc;
@@ -392,10 +416,10 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_apply(KParams p, int use_
     const int64_t tile = blockIdx.x;
     if (tile >= p.tile_off[p.nseq]) return;
     const int s = find_seg(p.tile_off, p.nseq, tile);
-    const int64_t c0 = p.chunk_off[s] + (tile - p.tile_off[s]) * p.group;
-    const int64_t c1 = min((int64_t)p.chunk_off[s + 1], c0 + p.group);
+    const int64_t c0 = p.sub_off[s] + (tile - p.tile_off[s]) * p.group;
+    const int64_t c1 = min((int64_t)p.sub_off[s + 1], c0 + p.group);
     const int e = blockIdx.y * kScanThreads + threadIdx.x;
-    float *st = p.states + (int64_t)h * p.nchunk_ub * (D * D) + e;
+    float *st = p.states + (int64_t)h * p.nsub_ub * (D * D) + e;
     float run = use_tiles ? p.tilesum[((int64_t)h * p.ntile_ub + tile) * (D * D) + e] : 0.f;
     if (p.s_init) run += p.s_init[((int64_t)s * p.heads + h) * (D * D) + e];   // carried-in state
     for (int64_t c = c0; c < c1; ++c) {
@@ -447,7 +471,7 @@ __global__ __launch_bounds__(512, 1) void k_fused(KParams p) {
     f32x4_t S[C::SA][C::SB];
     float *const fdst = final_state_dst<D>(p, s, h, gch);
     {
-        const float *src = chunk_start_state<D>(p, s, h, gch, cl);
+        const float *src = chunk_start_state<D>(p, s, h, cl);
 #pragma unroll
         for (int ia = 0; ia < C::SA; ++ia)
 #pragma unroll
@@ -781,13 +805,12 @@ __global__ __launch_bounds__(NW * 64, 1024 / (NW * 64)) void k_summary_reg(KPara
     Ring<2, SBY>::get(stages);
     const int h = blockIdx.y;
     const int gch = blockIdx.x;
-    if (gch >= p.chunk_off[p.nseq]) return;
-    const int s = find_seg(p.chunk_off, p.nseq, gch);
-    // The exclusive prefix never uses the last chunk of a sequence.
-    if (gch + 1 == p.chunk_off[s + 1]) return;
+    if (gch >= p.sub_off[p.nseq]) return;
+    const int s = find_seg(p.sub_off, p.nseq, gch);
+    const int64_t t0 = sub_first_token(p, s, gch);
+    if (t0 < 0) return;                              // in the sequence's last chunk: not needed
     const Unit u = unit_of<D>(p, s, h);
-    const int64_t t0 = (int64_t)(gch - p.chunk_off[s]) * p.chunk;
-    const int n = (int)min(u.len - t0, p.chunk);     // tokens of this chunk
+    const int n = (int)min(u.len - t0, p.sub);       // tokens of this sub-chunk
     const int64_t cb = (u.base + t0 * D) * 2;
     const uint32_t nbytes = (uint32_t)n * RB;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const char *>(p.k) + cb, nbytes);
@@ -890,7 +913,7 @@ __global__ __launch_bounds__(NW * 64, 1024 / (NW * 64)) void k_summary_reg(KPara
         }
     }
     wait_vm_lgkm0<0>();
-    float *dst = p.states + ((int64_t)h * p.nchunk_ub + gch) * (D * D);
+    float *dst = p.states + ((int64_t)h * p.nsub_ub + gch) * (D * D);
 #pragma unroll
     for (int ia = 0; ia < C::SA; ++ia)
 #pragma unroll
@@ -1141,7 +1164,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     if constexpr (LA >= 3) issue(1, stages[1]);
     float *const fdst = final_state_dst<D>(p, s, h, gch);
     {
-        const float *src = chunk_start_state<D>(p, s, h, gch, cl);
+        const float *src = chunk_start_state<D>(p, s, h, cl);
 #pragma unroll
         for (int ia = 0; ia < C::SA; ++ia)
 #pragma unroll
@@ -1304,10 +1327,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
             }
         }
 
-        // rotate the next tile's keys (its DMA was requested a tile ago) while
-        // the other waves are still on this tile's products; the barrier at
-        // the end of the tile publishes them
-        if constexpr (ROPE) rot_k(stages[(J + 1) % NST], t + 1);
+        // rotate the next tile's keys while the other waves are still on this
+        // tile's products; the barrier at the end of the tile publishes them.
+        // Not in a block's last tile: there the next tile's DMA is the newest
+        // request, and waiting for it here would drain the queue, so the
+        // rotation follows the tile's own wait instead.
+        if constexpr (ROPE && !last) rot_k(stages[(J + 1) % NST], t + 1);
 
         const char *ka[C::SA];
         const char *vbs[C::SB];
@@ -1341,7 +1366,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
 #pragma unroll
                     for (int kc = 0; kc < C::KC; ++kc) Q[si][kc] = Qn[si][kc];
             }
+            if constexpr (ROPE) rot_k(stages[(J + 1) % NST], t + 1);
             if constexpr (LA > 1) issue(t + LA, stages[(J + LA) % NST]);
+            if constexpr (ROPE) wait_vm_lgkm0<63>();     // the rotated tile is written
         } else {
             if (more || fdst) state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
             // DMA(t+1) has landed; younger are DMA(t+2 .. t+LA) and the Q
@@ -1377,6 +1404,7 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
         if (ev) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), st);
     };
     const dim3 gchunks((unsigned)plan.nchunk_ub, (unsigned)kp.heads);
+    const dim3 gsubs((unsigned)plan.nsub_ub, (unsigned)kp.heads);
     mark(0);
     hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, st, kp);
     if (kp.s_final) hipLaunchKernelGGL(k_state_empty<D>, dim3(kp.nseq, kp.heads), dim3(256), 0, st, kp);
@@ -1385,9 +1413,9 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
     // the chunk summaries before it; with one chunk per sequence there is none.
     if (!plan.single_chunk) {
         if constexpr (sizeof(T) == 2)
-            hipLaunchKernelGGL((k_summary_reg<D, BLK, 8, ROPE>), gchunks, dim3(512), 0, st, kp);
+            hipLaunchKernelGGL((k_summary_reg<D, BLK, 8, ROPE>), gsubs, dim3(512), 0, st, kp);
         else
-            hipLaunchKernelGGL((k_summary<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
+            hipLaunchKernelGGL((k_summary<T, D, BLK>), gsubs, dim3(512), 0, st, kp);
     }
     mark(2);
     if (!plan.single_chunk) {
@@ -1441,12 +1469,15 @@ int launch_fwd(const FwdArgs &a, void *stream, void *const *events) {
     kp.q = a.q; kp.k = a.k; kp.v = a.v; kp.o = a.o;
     kp.cu = a.cu_seqlens;
     kp.chunk_off = reinterpret_cast<int32_t *>(a.workspace + a.plan.off_chunk_off);
+    kp.sub_off = reinterpret_cast<int32_t *>(a.workspace + a.plan.off_sub_off);
     kp.tile_off = reinterpret_cast<int32_t *>(a.workspace + a.plan.off_tile_off);
     kp.states = reinterpret_cast<float *>(a.workspace + a.plan.off_states);
     kp.tilesum = reinterpret_cast<float *>(a.workspace + a.plan.off_tilesum);
     kp.seq_len = a.seq_len;
     kp.chunk = a.plan.chunk;
+    kp.sub = a.plan.sub;
     kp.nchunk_ub = a.plan.nchunk_ub;
+    kp.nsub_ub = a.plan.nsub_ub;
     kp.ntile_ub = a.plan.ntile_ub;
     kp.nseq = a.nseq;
     kp.heads = a.heads;

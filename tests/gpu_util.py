@@ -47,20 +47,23 @@ def host(x):
 
 
 class chunk_tokens:
-    """Temporarily force the library's chunk length (LA_CHUNK_TOKENS)."""
+    """Temporarily force the library's chunk length (LA_CHUNK_TOKENS) and,
+    optionally, its sub-chunk (summary) length (LA_SUB_TOKENS)."""
 
-    def __init__(self, n):
-        self.n = n
+    def __init__(self, n, sub=0):
+        self.vals = {"LA_CHUNK_TOKENS": n, "LA_SUB_TOKENS": sub}
 
     def __enter__(self):
-        self.old = os.environ.get("LA_CHUNK_TOKENS")
-        if self.n:
-            os.environ["LA_CHUNK_TOKENS"] = str(self.n)
-        else:
-            os.environ.pop("LA_CHUNK_TOKENS", None)
+        self.old = {k: os.environ.get(k) for k in self.vals}
+        for k, v in self.vals.items():
+            if v:
+                os.environ[k] = str(v)
+            else:
+                os.environ.pop(k, None)
 
     def __exit__(self, *a):
-        if self.old is None:
-            os.environ.pop("LA_CHUNK_TOKENS", None)
-        else:
-            os.environ["LA_CHUNK_TOKENS"] = self.old
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v

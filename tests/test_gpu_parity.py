@@ -45,13 +45,17 @@ def test_random_small(dev, dt, d, B, n):
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("B,C,n", [(64, 64, 64 * 40 + 7), (256, 256, 256 * 34 + 100),
-                                   (128, 512, 5000), (256, 1024, 3000)])
-def test_multi_chunk_and_scan_tiles(dev, dt, d, B, C, n):
-    """Forced chunk lengths: many chunks per sequence (> 32 runs the tiled scan)."""
-    note(f"multi_chunk dt={dt} d={d} B={B} C={C} n={n}")
+@pytest.mark.parametrize("B,C,S,n", [(64, 64, 0, 64 * 40 + 7), (256, 256, 0, 256 * 34 + 100),
+                                     (128, 512, 0, 5000), (256, 1024, 0, 3000),
+                                     (64, 256, 64, 64 * 40 + 7), (256, 1024, 256, 256 * 34 + 100),
+                                     (128, 2048, 512, 5000)])
+def test_multi_chunk_and_scan_tiles(dev, dt, d, B, C, S, n):
+    """Forced chunk lengths: many chunks per sequence (> 32 runs the tiled scan);
+    S > 0 also forces the summary sub-chunk, so a chunk starts from the prefix
+    of several sub-chunk summaries."""
+    note(f"multi_chunk dt={dt} d={d} B={B} C={C} S={S} n={n}")
     q, k, v = randn_qkv((1, 2, n, d), dt, 7 * n + d, dev)
-    with chunk_tokens(C):
+    with chunk_tokens(C, S):
         o = host(_fwd(q, k, v, B))
     ref = oracle.causal_linear_attention(host(q), host(k), host(v), "recurrent")
     assert oracle.rel_err(o, ref) <= TOL[dt]
@@ -74,15 +78,16 @@ def _onehot_inputs(rng, shape):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
-@pytest.mark.parametrize("d,B,n,C", [(64, 64, 1500, 0), (128, 256, 3000, 0), (128, 64, 2600, 64),
-                                     (64, 128, 4100, 128), (128, 128, 777, 0)])
-def test_integer_exact(dev, dt, d, B, n, C):
+@pytest.mark.parametrize("d,B,n,C,S", [(64, 64, 1500, 0, 0), (128, 256, 3000, 0, 0),
+                                       (128, 64, 2600, 64, 0), (64, 128, 4100, 128, 0),
+                                       (128, 128, 777, 0, 0), (128, 64, 2600, 512, 64)])
+def test_integer_exact(dev, dt, d, B, n, C, S):
     import torch
-    note(f"integer_exact dt={dt} d={d} B={B} n={n} C={C}")
+    note(f"integer_exact dt={dt} d={d} B={B} n={n} C={C} S={S}")
     rng = np.random.default_rng(n + d)
     qh, kh, vh = _onehot_inputs(rng, (2, 2, n, d))
     t = lambda x: torch.from_numpy(x).to(dev).to(torch_dtype(dt))
-    with chunk_tokens(C):
+    with chunk_tokens(C, S):
         o = host(_fwd(t(qh), t(kh), t(vh), B))
     ref = oracle.causal_linear_attention(qh, kh, vh, "naive")
     assert np.max(np.abs(ref)) <= 256
@@ -95,18 +100,19 @@ def test_one_hot_boundaries(dev):
     import torch
     n, d, B = 1100, 128, 256
     for j0 in (0, 255, 256, 511, 512, 1023, 1024, 1099):
-        note(f"one_hot j0={j0}")
-        q = torch.zeros((1, 1, n, d), dtype=torch.bfloat16, device=dev)
-        k = torch.zeros_like(q)
-        v = torch.zeros_like(q)
-        q[..., 5] = 1
-        k[0, 0, j0, 5] = 1
-        v[0, 0, j0, 77] = 1
-        with chunk_tokens(512):
-            o = host(_fwd(q, k, v, B))[0, 0]
-        expect = np.zeros((n, d), np.float32)
-        expect[j0:, 77] = 1
-        assert np.array_equal(o, expect), j0
+        for C, S in ((512, 0), (1024, 256)):
+            note(f"one_hot j0={j0} C={C} S={S}")
+            q = torch.zeros((1, 1, n, d), dtype=torch.bfloat16, device=dev)
+            k = torch.zeros_like(q)
+            v = torch.zeros_like(q)
+            q[..., 5] = 1
+            k[0, 0, j0, 5] = 1
+            v[0, 0, j0, 77] = 1
+            with chunk_tokens(C, S):
+                o = host(_fwd(q, k, v, B))[0, 0]
+            expect = np.zeros((n, d), np.float32)
+            expect[j0:, 77] = 1
+            assert np.array_equal(o, expect), (j0, C, S)
 
 
 # ----------------------------------------------------------------- packing
@@ -121,11 +127,11 @@ def test_varlen_matches_oracle(dev, dt, lengths):
     T, H, d = int(cu[-1]), 3, 128
     q, k, v = randn_qkv((H, T, d), dt, 31 + T, dev)
     cud = torch.from_numpy(cu).to(dev)
-    for C in (0, 256):
-        with chunk_tokens(C):
+    ref = oracle.causal_linear_attention_varlen(host(q), host(k), host(v), cu, "recurrent")
+    for C, S in ((0, 0), (256, 0), (1024, 256)):
+        with chunk_tokens(C, S):
             o = host(_fwd(q, k, v, 256, cud))
-        ref = oracle.causal_linear_attention_varlen(host(q), host(k), host(v), cu, "recurrent")
-        assert oracle.rel_err(o, ref) <= TOL[dt], C
+        assert oracle.rel_err(o, ref) <= TOL[dt], (C, S)
 
 
 def test_varlen_equals_separate_runs(dev):

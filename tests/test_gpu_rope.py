@@ -40,23 +40,25 @@ def _i32(x, dev):
 
 CASES = []
 for d in (64, 128):
-    for B, n, C in ((64, 1, 0), (256, 261, 0), (128, 3 * 128 + 7, 0), (64, 40 * 64 + 9, 128),
-                    (256, 9 * 256 + 100, 256)):
-        CASES.append((d, B, n, C))
+    for B, n, C, S in ((64, 1, 0, 0), (256, 261, 0, 0), (128, 3 * 128 + 7, 0, 0),
+                       (64, 40 * 64 + 9, 128, 0), (256, 9 * 256 + 100, 256, 0),
+                       (64, 40 * 64 + 9, 512, 128)):
+        CASES.append((d, B, n, C, S))
 
 
-@pytest.mark.parametrize("d,B,n,C", CASES)
+@pytest.mark.parametrize("d,B,n,C,S", CASES)
 @pytest.mark.parametrize("base", [1e4, 1e7])
-def test_rope_prefill_dense(dev, d, B, n, C, base):
-    """Dense input, zero and nonzero position offsets, initial and final states."""
+def test_rope_prefill_dense(dev, d, B, n, C, S, base):
+    """Dense input, zero and nonzero position offsets, initial and final
+    states; one chunk, many chunks, chunks of several summary sub-chunks."""
     import torch
     import linear_attention_attn_amd as la
-    note(f"rope dense d={d} B={B} n={n} C={C} base={base}")
+    note(f"rope dense d={d} B={B} n={n} C={C} S={S} base={base}")
     q, k, v = randn_qkv((2, 3, n, d), "bf16", 7000 + n + d + B, dev)
     off = [0, 123457]
     S0 = _states((2, 3, d, d), 71 + d, dev)
     Sf = torch.empty_like(S0)
-    with chunk_tokens(C):
+    with chunk_tokens(C, S):
         o = la.fwd(q, k, v, block_size=B, rope_dims=d // 2, rope_base=base,
                    pos_offset=_i32(off, dev), s_init=S0, s_final=Sf)
         torch.cuda.synchronize()

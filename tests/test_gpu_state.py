@@ -36,20 +36,22 @@ def _run(q, k, v, B, s_init, s_final, cu=None):
 CASES = []
 for dt in ("bf16", "f32"):
     for d in (64, 128):
-        for B, n, C in ((64, 1, 0), (256, 261, 0), (256, 3 * 256 + 7, 0), (64, 40 * 64 + 9, 128),
-                        (256, 34 * 256 + 100, 256)):
-            CASES.append((dt, d, B, n, C))
+        for B, n, C, S in ((64, 1, 0, 0), (256, 261, 0, 0), (256, 3 * 256 + 7, 0, 0),
+                           (64, 40 * 64 + 9, 128, 0), (256, 34 * 256 + 100, 256, 0),
+                           (64, 40 * 64 + 9, 512, 128)):
+            CASES.append((dt, d, B, n, C, S))
 
 
-@pytest.mark.parametrize("dt,d,B,n,C", CASES)
-def test_state_in_and_out(dev, dt, d, B, n, C):
-    """One chunk per sequence (C = 0, planned) and many chunks (forced C)."""
+@pytest.mark.parametrize("dt,d,B,n,C,S", CASES)
+def test_state_in_and_out(dev, dt, d, B, n, C, S):
+    """One chunk per sequence (C = 0, planned), many chunks (forced C), and
+    chunks of several summary sub-chunks (forced S)."""
     import torch
-    note(f"state dt={dt} d={d} B={B} n={n} C={C}")
+    note(f"state dt={dt} d={d} B={B} n={n} C={C} S={S}")
     q, k, v = randn_qkv((2, 3, n, d), dt, 3000 + n + d + B, dev)
     S0 = _states((2, 3, d, d), 77 + d, dev)
     Sf = torch.empty_like(S0)
-    with chunk_tokens(C):
+    with chunk_tokens(C, S):
         o = host(_run(q, k, v, B, S0, Sf))
     ref, sref = oracle.causal_linear_attention_state(host(q), host(k), host(v), host(S0))
     assert oracle.rel_err(o, ref) <= TOL[dt]
