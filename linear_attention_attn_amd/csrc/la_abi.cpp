@@ -56,9 +56,11 @@ static int64_t env_i64(const char *name, int64_t dflt) {
 // one workgroup per CU) with sub-chunks of 16384, so the summaries read 3/4
 // of k and v instead of 63/64 with 16384-token chunks.
 //
-// Packed input: C = C_s = the largest power of two <= W / kCUs (W = all
-// head-tokens), at most kSub, so there are at least about kCUs chunks and a
-// long sequence does not hold one CU for much longer than the others.
+// Packed input (the lengths live on the device): C = the largest power of
+// two <= W / kCUs (W = all head-tokens), so that there are at least about
+// kCUs chunks and no chunk is longer than a CU's average share; sub-chunks of
+// at most kSub.  The fused kernel takes the chunks of the longest sequences
+// first, so the long ones do not start last.
 //
 // LA_CHUNK_TOKENS forces C (a multiple of the block size, and of kSub above
 // it); LA_SUB_TOKENS forces C_s (a multiple of the block size dividing C).
@@ -97,7 +99,7 @@ void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int bloc
         const int64_t lavg = std::max<int64_t>(1, seq_len / batch);
         const int64_t per_cu = std::max<int64_t>(1, units * lavg / kCUs);
         C = B;
-        while (C * 2 <= kSub && C * 2 <= per_cu) C *= 2;
+        while (C * 2 <= cap && C * 2 <= per_cu) C *= 2;
     }
     const int64_t forced = env_i64("LA_CHUNK_TOKENS", 0);
     if (forced > 0) {
@@ -133,6 +135,12 @@ void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int bloc
     off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));
     p.off_sub_off = off;
     off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));
+    if (varlen) {
+        p.off_perm = off;
+        off = align256(off + (size_t)batch * sizeof(int32_t));
+        p.off_rank_off = off;
+        off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));
+    }
     p.off_tile_off = off;
     off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));
     p.off_states = off;

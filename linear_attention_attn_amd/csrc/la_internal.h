@@ -24,6 +24,8 @@ struct FwdPlan {
     bool single_chunk = false;  // every sequence is one chunk: no summaries, no scan
     size_t off_chunk_off = 0; // int32 [nseq + 1]
     size_t off_sub_off = 0;   // int32 [nseq + 1]
+    size_t off_perm = 0;      // int32 [nseq] (packed input: sequences longest first)
+    size_t off_rank_off = 0;  // int32 [nseq + 1]
     size_t off_tile_off = 0;  // int32 [nseq + 1]
     size_t off_states = 0;    // fp32 [heads][nsub_ub][d][d]
     size_t off_tilesum = 0;   // fp32 [heads][ntile_ub][d][d]

@@ -38,6 +38,11 @@ struct KParams {
     void *o;
     const int32_t *cu;      // packed offsets, or nullptr (dense)
     int32_t *chunk_off;     // [nseq + 1] chunks before each sequence
+    // longest-first order of the chunk workgroups (packed input; nullptr for
+    // dense): perm[r] = sequence of length rank r, rank_off[r] = chunks of the
+    // sequences ranked before r
+    int32_t *perm;          // [nseq]
+    int32_t *rank_off;      // [nseq + 1]
     int32_t *sub_off;       // [nseq + 1] sub-chunks before each sequence
     int32_t *tile_off;      // [nseq + 1] scan tiles before each sequence
     float *states;          // [heads][nsub_ub][D*D]
@@ -93,6 +98,28 @@ __device__ __forceinline__ int find_seg(const int32_t *off, int n, int64_t x) {
     return lo;
 }
 
+// The (head, chunk, sequence) of a chunk workgroup, or false when the
+// workgroup has no chunk.  Workgroups are taken in dispatch order with the
+// head varying fastest, so all heads of one chunk slot start together; with
+// a ranking (packed input) the slots go to the chunks of the longest
+// sequences first, so that a long sequence's chunks do not start last and
+// hold a few CUs after the others have finished.
+__device__ __forceinline__ bool chunk_of_block(const KParams &p, int &h, int64_t &gch, int &s) {
+    const int64_t lin = (int64_t)blockIdx.x + (int64_t)gridDim.x * blockIdx.y;
+    h = (int)(lin % p.heads);
+    const int64_t slot = lin / p.heads;
+    if (slot >= p.chunk_off[p.nseq]) return false;
+    if (p.perm != nullptr) {
+        const int r = find_seg(p.rank_off, p.nseq, slot);
+        s = p.perm[r];
+        gch = p.chunk_off[s] + (slot - p.rank_off[r]);
+    } else {
+        gch = slot;
+        s = find_seg(p.chunk_off, p.nseq, gch);
+    }
+    return true;
+}
+
 // Source of the state at the start of chunk cl (chunk-local index) of
 // sequence s, head h, or nullptr for zero: the scanned prefix in `states` at
 // the chunk's first sub-chunk (which includes a carried-in initial state when
@@ -136,6 +163,7 @@ __global__ __launch_bounds__(256) void k_state_empty(KParams p) {
 // chunk_off[s] = sum_{s' < s} ceil(L_s' / C), sub_off[s] = sum ceil(L_s' / C_s),
 // tile_off[s] = sum ceil(ns_s' / G) (ns = sub-chunks of a sequence).
 constexpr int kPrepThreads = 1024;
+constexpr int kSortMax = 4096;   // sequences ranked by length for the fused grid
 
 __global__ __launch_bounds__(kPrepThreads) void k_prep(KParams p) {
     __shared__ int64_t sc[kPrepThreads], su[kPrepThreads], st[kPrepThreads];
@@ -178,6 +206,61 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(KParams p) {
         p.sub_off[p.nseq] = (int32_t)su[t];
         p.tile_off[p.nseq] = (int32_t)st[t];
     }
+    if (p.perm == nullptr) return;
+
+    // Longest-first ranking of the sequences (bitonic sort of (length, index)
+    // keys in LDS, up to kSortMax sequences; beyond that the natural order),
+    // then rank_off = exclusive prefix of the chunk counts in rank order.
+    __shared__ uint64_t key[kSortMax];
+    const int n = p.nseq;
+    const bool sorted = n <= kSortMax;
+    if (sorted) {
+        int np2 = 1;
+        while (np2 < n) np2 <<= 1;
+        for (int i = t; i < np2; i += kPrepThreads) {
+            const int64_t L = i < n ? (int64_t)p.cu[i + 1] - p.cu[i] : 0;
+            key[i] = i < n ? ((uint64_t)(INT32_MAX - L) << 32) | (uint32_t)i : ~0ull;
+        }
+        __syncthreads();
+        for (int k = 2; k <= np2; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int i = t; i < np2; i += kPrepThreads) {
+                    const int ixj = i ^ j;
+                    if (ixj > i) {
+                        const uint64_t a = key[i], b = key[ixj];
+                        if ((a > b) == ((i & k) == 0)) { key[i] = b; key[ixj] = a; }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+    }
+    auto seq_at = [&](int r) { return sorted ? (int)(uint32_t)key[r] : r; };
+    int64_t cr = 0;
+    for (int r = s0; r < s1; ++r) {
+        int64_t nc, ns, ng;
+        counts(seq_at(r), nc, ns, ng);
+        cr += nc;
+    }
+    __syncthreads();
+    sc[t] = cr;
+    __syncthreads();
+    for (int d = 1; d < kPrepThreads; d <<= 1) {
+        const int64_t a = t >= d ? sc[t - d] : 0;
+        __syncthreads();
+        sc[t] += a;
+        __syncthreads();
+    }
+    cr = t ? sc[t - 1] : 0;
+    for (int r = s0; r < s1; ++r) {
+        const int sq = seq_at(r);
+        p.perm[r] = sq;
+        p.rank_off[r] = (int32_t)cr;
+        int64_t nc, ns, ng;
+        counts(sq, nc, ns, ng);
+        cr += nc;
+    }
+    if (t == kPrepThreads - 1) p.rank_off[n] = (int32_t)sc[t];
 }
 
 // ---------------------------------------------------------- tile config
@@ -450,10 +533,9 @@ __global__ __launch_bounds__(512, 1) void k_fused(KParams p) {
     __shared__ __attribute__((aligned(16))) char lds[NBUF * BUF + C::ST_BYTES];
     char *const st = lds + NBUF * BUF;
 
-    const int h = blockIdx.y;
-    const int64_t gch = blockIdx.x;
-    if (gch >= p.chunk_off[p.nseq]) return;
-    const int s = find_seg(p.chunk_off, p.nseq, gch);
+    int h, s;
+    int64_t gch;
+    if (!chunk_of_block(p, h, gch, s)) return;
     const Unit u = unit_of<D>(p, s, h);
     const int64_t cl = gch - p.chunk_off[s];
     const int64_t t0 = cl * p.chunk;
@@ -1003,10 +1085,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     char *stages[NST];
     Ring<NST, SBY>::get(stages);
 
-    const int h = blockIdx.y;
-    const int gch = blockIdx.x;
-    if (gch >= p.chunk_off[p.nseq]) return;
-    const int s = find_seg(p.chunk_off, p.nseq, gch);
+    int h, s;
+    int64_t gch;
+    if (!chunk_of_block(p, h, gch, s)) return;
     const Unit u = unit_of<D>(p, s, h);
     const int cl = gch - p.chunk_off[s];
     const int64_t t0 = (int64_t)cl * p.chunk;
@@ -1470,6 +1551,8 @@ int launch_fwd(const FwdArgs &a, void *stream, void *const *events) {
     kp.cu = a.cu_seqlens;
     kp.chunk_off = reinterpret_cast<int32_t *>(a.workspace + a.plan.off_chunk_off);
     kp.sub_off = reinterpret_cast<int32_t *>(a.workspace + a.plan.off_sub_off);
+    kp.perm = a.cu_seqlens ? reinterpret_cast<int32_t *>(a.workspace + a.plan.off_perm) : nullptr;
+    kp.rank_off = a.cu_seqlens ? reinterpret_cast<int32_t *>(a.workspace + a.plan.off_rank_off) : nullptr;
     kp.tile_off = reinterpret_cast<int32_t *>(a.workspace + a.plan.off_tile_off);
     kp.states = reinterpret_cast<float *>(a.workspace + a.plan.off_states);
     kp.tilesum = reinterpret_cast<float *>(a.workspace + a.plan.off_tilesum);

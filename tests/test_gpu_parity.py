@@ -134,6 +134,24 @@ def test_varlen_matches_oracle(dev, dt, lengths):
         assert oracle.rel_err(o, ref) <= TOL[dt], (C, S)
 
 
+@pytest.mark.parametrize("nseq", [4096, 4097])
+def test_varlen_many_sequences(dev, nseq):
+    """Many short packed sequences (0 to 70 tokens): up to 4096 the fused
+    grid takes them longest first, beyond that in their own order."""
+    import torch
+    note(f"varlen many nseq={nseq}")
+    rng = np.random.default_rng(nseq)
+    lengths = rng.integers(0, 71, size=nseq)
+    lengths[rng.integers(0, nseq, size=50)] = 0
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T, H, d = int(cu[-1]), 2, 64
+    q, k, v = randn_qkv((H, T, d), "bf16", nseq, dev)
+    cud = torch.from_numpy(cu).to(dev)
+    o = host(_fwd(q, k, v, 64, cud))
+    ref = oracle.causal_linear_attention_varlen(host(q), host(k), host(v), cu, "recurrent")
+    assert oracle.rel_err(o, ref) <= TOL["bf16"]
+
+
 def test_varlen_equals_separate_runs(dev):
     import torch
     lengths = (700, 1, 2500, 256, 0, 1300)
