@@ -147,6 +147,49 @@ def bench_prefill(w, steps, warmup, dev, traced=True):
     return (t1 - t0) * 1000.0 / steps, stage, chunk, nbytes
 
 
+def bench_prefill_varlen(w, steps, warmup, dev):
+    """The packed workload (sequences of the log-uniform lengths back to back,
+    cu_seqlens offsets) through lightning_attn_fwd_traced; returns (ms per
+    step, per-kernel ms, chunk tokens, total tokens)."""
+    import torch
+    import linear_attention_attn_amd as la
+    import synth
+
+    lengths = synth.varlen_lengths(w.batch, w.len_seed)
+    q, k, v, cu = synth.varlen_inputs(lengths, w.heads, w.head_dim, w.dtype, w.cid, dev)
+    T = int(cu[-1])
+    cud = torch.tensor(cu, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    code = la.LA_DTYPE_BF16 if w.dtype == "bf16" else la.LA_DTYPE_F32
+    nbytes = la.lightning_attn_fwd_workspace_size(w.batch, w.heads, T, w.head_dim, w.block_size, 1, code)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    args = (q, k, v, o, w.batch, w.heads, T, w.head_dim, w.block_size, cud, code, ws, nbytes, stream)
+    for _ in range(warmup):
+        st = la.lightning_attn_fwd(*args)
+        if st != la.LA_OK:
+            raise la.LightningAttnError(st, "lightning_attn_fwd")
+    torch.cuda.synchronize()
+    hip = HipEvents()
+    evs = [hip.create(la.LA_FWD_NUM_EVENTS) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        st = la.lightning_attn_fwd_traced(*args, evs[i], la.LA_FWD_NUM_EVENTS)
+        if st != la.LA_OK:
+            raise la.LightningAttnError(st, "lightning_attn_fwd_traced")
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    names = ["tables", "summary", "scan", "fused"]
+    stage = {n: sum(hip.ms(e[j], e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
+    for e in evs:
+        hip.destroy(e)
+    chunk = la.lightning_attn_fwd_chunk_tokens(w.batch, w.heads, T, w.head_dim, w.block_size, 1, code)
+    del q, k, v, o, ws, cud
+    torch.cuda.empty_cache()
+    return (t1 - t0) * 1000.0 / steps, stage, chunk, T
+
+
 def bench_prefill_state(w, steps, warmup, dev, rope=False):
     """The prefill workload through lightning_attn_fwd_state, each sequence
     starting from a state and returning its final state (in place); with
@@ -479,6 +522,20 @@ def main():
                           "kernels_ms": lstage, "chunk_tokens": lchunk}
         out["long_1m"]["mfma_frac"] = out["long_1m"]["tflops"] / PEAK_BF16_TFLOPS
         log(json.dumps(out["long_1m"]))
+        wv = synth.WORKLOADS["varlen16"]
+        log(f"prefill {wv.name}: {wv.note}")
+        vms, vstage, vchunk, vT = bench_prefill_varlen(wv, 10, 5, dev)
+        vht = wv.heads * vT
+        vbytes = vht * 4 * wv.head_dim * 2
+        out["varlen16"] = {"workload": f"{wv.note}, H{wv.heads} d{wv.head_dim}, block {wv.block_size}, "
+                                       f"{vT} tokens",
+                           "ms_per_step": vms, "tokens_per_s": vT / (vms * 1e-3),
+                           "tflops": vht * prefill_flops_per_head_token(wv.head_dim, wv.block_size)
+                           / (vms * 1e-3) / 1e12,
+                           "hbm_gbs": vbytes / (vms * 1e-3) / 1e9,
+                           "roofline_frac": vbytes / (PEAK_HBM_GBS * 1e9) / (vms * 1e-3),
+                           "kernels_ms": vstage, "chunk_tokens": vchunk}
+        log(json.dumps(out["varlen16"]))
 
     if args.copy_calibration:
         out["copy_calibration"] = copy_calibration(dev)
