@@ -200,6 +200,34 @@ int lightning_attn_fwd_rope(const void *q, const void *k, const void *v, void *o
                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Prefill over an indexed state table, for serving loops that keep every
+ * live sequence's state in a pool (the wiki page's section "计算优化" lists
+ * separate prefill and decoding execution and multi-level padding among the
+ * inference optimisations): sequence s starts from pool entry slots[s] and
+ * its state after its last token is written back to that entry, so a prompt
+ * can be prefilled in pieces between decode steps
+ * (lightning_attn_decode_indexed / lightning_attn_decode_rope on the same
+ * pool) without gathering or scattering states.
+ *   state_pool: fp32 [nslots][heads][head_dim][head_dim] (decode layout), read
+ *               and updated in place; may be NULL only when nslots == 0;
+ *   slots:      DEVICE int32 [batch] (required); a slot < 0 or >= nslots makes
+ *               the sequence stateless: it starts from zero and its final
+ *               state is dropped (padding, or a one-shot prefill).  Two
+ *               sequences must not name the same slot (precondition, not
+ *               checked).  A sequence of length 0 leaves its entry unchanged.
+ *   rope_dims:  0 (no rotation) or head_dim / 2 with rope_base and pos_offset
+ *               as in lightning_attn_fwd_rope (then dtype must be bf16).
+ * Everything else (layouts, cu_seqlens, workspace, checks) is as
+ * lightning_attn_fwd.  Then o_i = q_i (S_slot + sum_{j <= i} k_j^T v_j).
+ */
+int lightning_attn_fwd_indexed(const void *q, const void *k, const void *v, void *o,
+                               int batch, int heads, int64_t seq_len, int head_dim, int block_size,
+                               const int32_t *cu_seqlens, int dtype,
+                               float *state_pool, int nslots, const int32_t *slots,
+                               int rope_dims, double rope_base, const int32_t *pos_offset,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One decode step with q and k rotated as in lightning_attn_fwd_rope, row b
  * at position positions[b] (DEVICE int32 [batch], required).  With slots ==
  * NULL the states are [batch][heads][head_dim][head_dim] (as

@@ -24,6 +24,7 @@ __all__ = [
     "lightning_attn_fwd_traced", "lightning_attn_decode", "lightning_attn_strerror", "fwd",
     "decode", "LA_FWD_NUM_EVENTS", "lightning_attn_fwd_state", "lightning_attn_fwd_rope",
     "lightning_attn_decode_indexed", "lightning_attn_decode_rope", "decode_indexed", "decode_rope",
+    "lightning_attn_fwd_indexed",
 ]
 
 LA_DTYPE_BF16 = 0
@@ -75,6 +76,9 @@ def load_library():
     lib.lightning_attn_fwd_rope.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, i32, i32,
                                             ctypes.c_double, vp, vp, vp, vp, sz, vp]
     lib.lightning_attn_fwd_rope.restype = i32
+    lib.lightning_attn_fwd_indexed.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, i32, vp,
+                                               i32, vp, i32, ctypes.c_double, vp, vp, sz, vp]
+    lib.lightning_attn_fwd_indexed.restype = i32
     lib.lightning_attn_decode_rope.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32,
                                                ctypes.c_double, vp, vp]
     lib.lightning_attn_decode_rope.restype = i32
@@ -127,6 +131,15 @@ def lightning_attn_fwd_rope(q, k, v, o, batch, heads, seq_len, head_dim, block_s
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, heads, seq_len, head_dim, block_size,
         _ptr(cu_seqlens), dtype, rope_dims, float(rope_base), _ptr(pos_offset), _ptr(s_init),
         _ptr(s_final), _ptr(workspace), workspace_bytes, stream))
+
+
+def lightning_attn_fwd_indexed(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens,
+                               dtype, state_pool, nslots, slots, rope_dims, rope_base, pos_offset,
+                               workspace, workspace_bytes, stream) -> int:
+    return int(load_library().lightning_attn_fwd_indexed(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, heads, seq_len, head_dim, block_size,
+        _ptr(cu_seqlens), dtype, _ptr(state_pool), nslots, _ptr(slots), rope_dims, float(rope_base),
+        _ptr(pos_offset), _ptr(workspace), workspace_bytes, stream))
 
 
 def lightning_attn_fwd_traced(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens,
@@ -191,7 +204,7 @@ def workspace_for(q, block_size: int, cu_seqlens=None):
 
 def fwd(q, k, v, block_size: int = 256, cu_seqlens=None, out=None, workspace=None,
         s_init=None, s_final=None, rope_dims: int = 0, rope_base: float = 10000.0,
-        pos_offset=None):
+        pos_offset=None, state_pool=None, slots=None):
     """Causal linear attention forward on the current stream.
 
     Dense: q, k, v [batch, heads, n, d].  Packed: q, k, v [heads, T, d] with
@@ -203,6 +216,10 @@ def fwd(q, k, v, block_size: int = 256, cu_seqlens=None, out=None, workspace=Non
     rope_dims > 0 (= d / 2, bf16 only): q and k rotated on the way in
     (lightning_attn_fwd_rope), token t of sequence s at position
     pos_offset[s] + t (pos_offset: int32 device tensor [nseq], or None for 0).
+    state_pool / slots: prefill over an indexed state table
+    (lightning_attn_fwd_indexed): sequence s starts from state_pool[slots[s]]
+    and its final state is written back there (fp32 [nslots, heads, d, d];
+    slots int32 device [nseq]); not combined with s_init / s_final.
     """
     import torch
     for t in (q, k, v):
@@ -231,7 +248,19 @@ def fwd(q, k, v, block_size: int = 256, cu_seqlens=None, out=None, workspace=Non
     if pos_offset is not None and (pos_offset.dtype != torch.int32 or not pos_offset.is_cuda
                                    or pos_offset.numel() != batch):
         raise ValueError("pos_offset must be an int32 device tensor of nseq entries")
-    if rope_dims:
+    if slots is not None:
+        if s_init is not None or s_final is not None:
+            raise ValueError("state_pool/slots and s_init/s_final are exclusive")
+        if slots.dtype != torch.int32 or not slots.is_cuda or slots.numel() != batch:
+            raise ValueError("slots must be an int32 device tensor of nseq entries")
+        if (state_pool.dtype != torch.float32 or not state_pool.is_contiguous()
+                or tuple(state_pool.shape[1:]) != (heads, d, d)):
+            raise ValueError("state_pool must be a contiguous fp32 tensor [nslots, heads, d, d]")
+        st = lightning_attn_fwd_indexed(q, k, v, o, batch, heads, n, d, block_size, cu, _dtype_code(q),
+                                        state_pool, state_pool.shape[0], slots, rope_dims, rope_base,
+                                        pos_offset, workspace if nbytes else None, nbytes,
+                                        _stream_handle(q.device))
+    elif rope_dims:
         st = lightning_attn_fwd_rope(q, k, v, o, batch, heads, n, d, block_size, cu, _dtype_code(q),
                                      rope_dims, rope_base, pos_offset, s_init, s_final,
                                      workspace if nbytes else None, nbytes, _stream_handle(q.device))

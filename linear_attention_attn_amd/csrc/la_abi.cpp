@@ -185,7 +185,8 @@ static int fwd_common(const void *q, const void *k, const void *v, void *o, int 
                       int64_t seq_len, int head_dim, int block_size, const int32_t *cu_seqlens,
                       int dtype, const float *s_init, float *s_final, void *workspace,
                       size_t workspace_bytes, void *stream, void *const *events,
-                      int rope_dims = 0, double rope_base = 0.0, const int32_t *pos0 = nullptr) {
+                      int rope_dims = 0, double rope_base = 0.0, const int32_t *pos0 = nullptr,
+                      const int32_t *slots = nullptr, int nslots = 0) {
     int st = la::check_fwd_shape(batch, heads, seq_len, head_dim, block_size, dtype);
     if (st != LA_OK) return st;
     if (rope_dims != 0 && dtype != LA_DTYPE_BF16) return LA_EUNSUPPORTED;
@@ -193,8 +194,9 @@ static int fwd_common(const void *q, const void *k, const void *v, void *o, int 
     if (st != LA_OK) return st;
     if (((uintptr_t)s_init & 15) != 0 || ((uintptr_t)s_final & 15) != 0) return LA_EINVAL;
     if (seq_len == 0) {
-        // no tokens: only the final states (each equal to its initial state)
-        if (!s_final) return LA_OK;
+        // no tokens: only the final states (each equal to its initial state;
+        // a pool entry is updated in place, so there is nothing to do)
+        if (!s_final || slots) return LA_OK;
         return la::launch_state_empty(s_init, s_final, batch, heads, head_dim, stream) == 0 ? LA_OK : LA_EHIP;
     }
     if (!q || !k || !v || !o) return LA_EINVAL;
@@ -204,6 +206,7 @@ static int fwd_common(const void *q, const void *k, const void *v, void *o, int 
     a.dtype = dtype; a.seq_len = seq_len; a.cu_seqlens = cu_seqlens;
     a.s_init = s_init; a.s_final = s_final;
     a.rope_dims = rope_dims; a.rope_base = rope_base; a.pos0 = pos0;
+    a.slots = slots; a.nslots = nslots;
     la::make_fwd_plan(batch, heads, seq_len, head_dim, block_size, cu_seqlens != nullptr, &a.plan);
     if (!workspace || workspace_bytes < a.plan.bytes) return LA_EWORKSPACE;
     if (((uintptr_t)workspace & 255) != 0) return LA_EINVAL;
@@ -236,6 +239,19 @@ int lightning_attn_fwd_rope(const void *q, const void *k, const void *v, void *o
     return fwd_common(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens, dtype,
                       s_init, s_final, workspace, workspace_bytes, stream, nullptr, rope_dims,
                       rope_base, pos_offset);
+}
+
+int lightning_attn_fwd_indexed(const void *q, const void *k, const void *v, void *o, int batch,
+                               int heads, int64_t seq_len, int head_dim, int block_size,
+                               const int32_t *cu_seqlens, int dtype, float *state_pool, int nslots,
+                               const int32_t *slots, int rope_dims, double rope_base,
+                               const int32_t *pos_offset, void *workspace, size_t workspace_bytes,
+                               void *stream) {
+    if (!slots || nslots < 0 || (nslots > 0 && !state_pool)) return LA_EINVAL;
+    if ((int64_t)nslots * heads > (int64_t)INT32_MAX) return LA_EUNSUPPORTED;
+    return fwd_common(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens, dtype,
+                      state_pool, state_pool, workspace, workspace_bytes, stream, nullptr, rope_dims,
+                      rope_base, pos_offset, slots, nslots);
 }
 
 int lightning_attn_fwd_traced(const void *q, const void *k, const void *v, void *o, int batch,

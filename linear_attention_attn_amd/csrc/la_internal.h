@@ -49,6 +49,8 @@ struct FwdArgs {
     const int32_t *cu_seqlens;  // device, or nullptr for dense input
     const float *s_init;      // device [nseq][heads][d][d] or nullptr (zero)
     float *s_final;           // device [nseq][heads][d][d] or nullptr (not wanted)
+    const int32_t *slots = nullptr;  // device [nseq]: with it s_init == s_final is a pool
+    int nslots = 0;                  // of nslots entries; sequence s uses entry slots[s]
     int rope_dims = 0;        // > 0: rotate the first rope_dims dims of q and k (bf16)
     double rope_base = 0.0;   // rotary base frequency
     const int32_t *pos0 = nullptr;  // device [nseq]: position of each first token, or nullptr (0)

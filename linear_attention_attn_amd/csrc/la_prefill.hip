@@ -56,9 +56,13 @@ struct KParams {
     // and final states of the same layout (or nullptr = not wanted).
     // init_mode 0: no initial state; 1: the scan adds it to every chunk's
     // prefix in `states`; 2: one chunk per sequence, read directly.
+    // With a slot table, s_init and s_final are one pool of nslots entries
+    // and sequence s uses entry slots[s] (none when out of range).
     const float *s_init;
     float *s_final;
     int init_mode;
+    const int32_t *slots;
+    int nslots;
     // rotary position embedding of q and k (bf16 kernels with ROPE set):
     // rope_dims rotated dims, base frequency, and the position of each
     // sequence's first token (pos0[s], or 0 when pos0 is nullptr)
@@ -120,13 +124,25 @@ __device__ __forceinline__ bool chunk_of_block(const KParams &p, int &h, int64_t
     return true;
 }
 
+// State entry of sequence s: s itself, or with a slot table slots[s]; -1 when
+// the slot is out of range (no state read or written: the sequence starts
+// from zero and its final state is dropped).
+__device__ __forceinline__ int64_t state_entry(const KParams &p, int s) {
+    if (p.slots == nullptr) return s;
+    const int sl = p.slots[s];
+    return (sl < 0 || sl >= p.nslots) ? -1 : sl;
+}
+
 // Source of the state at the start of chunk cl (chunk-local index) of
 // sequence s, head h, or nullptr for zero: the scanned prefix in `states` at
 // the chunk's first sub-chunk (which includes a carried-in initial state when
 // one was given), or with one chunk per sequence the initial state itself.
 template <int D>
 __device__ __forceinline__ const float *chunk_start_state(const KParams &p, int s, int h, int64_t cl) {
-    if (p.init_mode == 2) return p.s_init + ((int64_t)s * p.heads + h) * (D * D);
+    if (p.init_mode == 2) {
+        const int64_t e = state_entry(p, s);
+        return e < 0 ? nullptr : p.s_init + (e * p.heads + h) * (D * D);
+    }
     if (p.init_mode == 0 && cl == 0) return nullptr;
     const int64_t gsub = p.sub_off[s] + cl * (p.chunk / p.sub);
     return p.states + ((int64_t)h * p.nsub_ub + gsub) * (D * D);
@@ -145,10 +161,12 @@ __device__ __forceinline__ int64_t sub_first_token(const KParams &p, int s, int6
 template <int D>
 __device__ __forceinline__ float *final_state_dst(const KParams &p, int s, int h, int64_t gch) {
     if (p.s_final == nullptr || gch + 1 != p.chunk_off[s + 1]) return nullptr;
-    return p.s_final + ((int64_t)s * p.heads + h) * (D * D);
+    const int64_t e = state_entry(p, s);
+    return e < 0 ? nullptr : p.s_final + (e * p.heads + h) * (D * D);
 }
 
 // Final state of sequences with no tokens: the initial state (or zero).
+// (Not launched with a slot table: there the entry is updated in place.)
 template <int D>
 __global__ __launch_bounds__(256) void k_state_empty(KParams p) {
     const int s = blockIdx.x, h = blockIdx.y;
@@ -504,7 +522,10 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_apply(KParams p, int use_
     const int e = blockIdx.y * kScanThreads + threadIdx.x;
     float *st = p.states + (int64_t)h * p.nsub_ub * (D * D) + e;
     float run = use_tiles ? p.tilesum[((int64_t)h * p.ntile_ub + tile) * (D * D) + e] : 0.f;
-    if (p.s_init) run += p.s_init[((int64_t)s * p.heads + h) * (D * D) + e];   // carried-in state
+    if (p.s_init) {                                  // carried-in state
+        const int64_t se = state_entry(p, s);
+        if (se >= 0) run += p.s_init[(se * p.heads + h) * (D * D) + e];
+    }
     for (int64_t c = c0; c < c1; ++c) {
         const float x = st[c * (D * D)];
         st[c * (D * D)] = run;
@@ -1488,7 +1509,8 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
     const dim3 gsubs((unsigned)plan.nsub_ub, (unsigned)kp.heads);
     mark(0);
     hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, st, kp);
-    if (kp.s_final) hipLaunchKernelGGL(k_state_empty<D>, dim3(kp.nseq, kp.heads), dim3(256), 0, st, kp);
+    if (kp.s_final && !kp.slots)
+        hipLaunchKernelGGL(k_state_empty<D>, dim3(kp.nseq, kp.heads), dim3(256), 0, st, kp);
     mark(1);
     // Every chunk but the first of its sequence needs the exclusive prefix of
     // the chunk summaries before it; with one chunk per sequence there is none.
@@ -1567,7 +1589,9 @@ int launch_fwd(const FwdArgs &a, void *stream, void *const *events) {
     kp.group = a.plan.scan_group;
     kp.s_init = a.s_init;
     kp.s_final = a.s_final;
-    kp.init_mode = a.s_init == nullptr ? 0 : (a.plan.single_chunk ? 2 : 1);
+    kp.slots = a.slots;
+    kp.nslots = a.nslots;
+    kp.init_mode = (a.s_init == nullptr && a.slots == nullptr) ? 0 : (a.plan.single_chunk ? 2 : 1);
     kp.pos0 = a.pos0;
     kp.rope_base = a.rope_base;
     kp.rope_dims = a.rope_dims;

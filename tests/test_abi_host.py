@@ -132,6 +132,25 @@ def test_rope_rejects(la):
     assert dr(128, 5, 64, 1e4) == 2
 
 
+def test_fwd_indexed_rejects(la):
+    """The indexed prefill's own arguments are checked before any launch."""
+    fake = 1 << 20
+    need = la.lightning_attn_fwd_workspace_size(2, 1, 10, 128, 64, 1, 0)
+
+    def fi(pool=fake, nslots=3, slots=fake, dt=0, r=0, base=1e4):
+        return la.lightning_attn_fwd_indexed(fake, fake, fake, fake, 2, 1, 10, 128, 64, fake, dt, pool,
+                                             nslots, slots, r, base, None, fake, need, None)
+    assert fi(slots=None) == 1               # the slot table is required
+    assert fi(nslots=-1) == 1
+    assert fi(pool=None) == 1                # a pool is needed when it has entries
+    assert fi(dt=1, r=64) == 2               # rotation: bf16 only
+    assert fi(r=32) == 2                     # rotation: half the head dims only
+    assert fi(r=64, base=0.0) == 1
+    assert fi(pool=fake + 4) == 1            # 16-byte alignment
+    assert la.lightning_attn_fwd_indexed(fake, fake, fake, fake, 2, 1, 0, 128, 64, fake, 0, None, 0, fake,
+                                         0, 1e4, None, None, 0, None) == 0   # no tokens: nothing to do
+
+
 def test_product_never_imports_oracle():
     """The HIP path must not route through the CPU oracle."""
     pkg = os.path.join(ROOT, "linear_attention_attn_amd")
