@@ -54,7 +54,7 @@ struct KParams {
     int nseq, heads, group;
     // state handoff: initial states [nseq][heads][D][D] (or nullptr = zero)
     // and final states of the same layout (or nullptr = not wanted).
-    // init_mode 0: no initial state; 1: the scan adds it to every chunk's
+    // init_mode 0: no initial state; 1: the scan adds it to every sub-chunk's
     // prefix in `states`; 2: one chunk per sequence, read directly.
     // With a slot table, s_init and s_final are one pool of nslots entries
     // and sequence s uses entry slots[s] (none when out of range).
@@ -883,9 +883,9 @@ __device__ __forceinline__ RopeK rope_k_lane(int w, int l) {
     return r;
 }
 
-// U_c = K_c^T V_c over a chunk, with the K/V tiles staged through
+// U_c = K_c^T V_c over a sub-chunk, with the K/V tiles staged through
 // registers: each wave loads its 16-byte pieces of tile t + 2 into registers
-// (buffer loads, rows past the chunk end read as zeros) while tile t is
+// (buffer loads, rows past the sub-chunk end read as zeros) while tile t is
 // summed, and writes tile t + 1 into the other LDS stage at the end of tile
 // t.  Same LDS layout as the fused kernel's tiles.  Measured on MI355X,
 // buffer-to-LDS loads alone stream at most ~6.3 TB/s and register loads
