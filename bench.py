@@ -420,14 +420,16 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="only the headline prefill workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--workload", default="minimax_layer")
+    ap.add_argument("--workload", default="minimax_layer",
+                    choices=["minimax_layer", "long_1m", "tiny_f32"],
+                    help="dense prefill workload of the headline line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also time a plain 1 GiB device copy (the reference kernel for the "
                          "HBM byte counters) and report its GB/s")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads shard with no communication; see the design notes). Run with --gpus 1.",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(heads shard with no communication). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
