@@ -1,0 +1,43 @@
+// Host-side check of the forward-pass plan (la_abi.cpp's make_fwd_plan) over
+// random shapes: chunk and sub-chunk lengths are multiples of the block size,
+// the chunk a multiple of the sub-chunk, sub-chunks at most 16384 tokens
+// (unless one chunk covers the sequence), chunk rows within 2^30 bytes, and the
+// slot counts match the dense shape.  Built with g++ against stubs of the
+// launchers; run by tests/test_plan_host.py.
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include "la_internal.h"
+namespace la {
+int launch_fwd(const FwdArgs &, void *, void *const *) { return 0; }
+int launch_state_empty(const float *, float *, int, int, int, void *) { return 0; }
+int launch_decode(const void *, const void *, const void *, float *, void *, int, int, int, int, void *,
+                  const int32_t *, int, int, double, const int32_t *) { return 0; }
+}
+int main() {  // exit status 0 when every plan passes
+    std::mt19937_64 rng(1);
+    long bad = 0, n = 0;
+    for (int it = 0; it < 200000; ++it) {
+        int batch = 1 + rng() % 300, heads = 1 + rng() % 128;
+        int d = (rng() & 1) ? 64 : 128, B = 64 << (rng() % 3);
+        bool varlen = rng() & 1;
+        int64_t L = 1 + (int64_t)(rng() % (1ull << (1 + rng() % 27)));
+        if (varlen) L = L * (1 + rng() % 4);
+        if (L > 2000000000LL) L = 2000000000LL;
+        la::FwdPlan p;
+        la::make_fwd_plan(batch, heads, L, d, B, varlen, &p);
+        ++n;
+        const int64_t cap = ((1LL << 30) / (d * 2)) / B * B;
+        bool ok = p.chunk >= B && p.chunk % B == 0 && p.chunk <= cap && p.sub >= B && p.sub % B == 0 &&
+                  p.chunk % p.sub == 0 && (p.sub <= 16384 || p.single_chunk) && p.bytes > 0;
+        if (!varlen) {
+            const int64_t cps = (L + p.chunk - 1) / p.chunk;
+            ok = ok && p.nchunk_ub == batch * cps && p.single_chunk == (cps == 1);
+        }
+        if (!ok && bad++ < 10)
+            printf("bad: b=%d h=%d L=%lld d=%d B=%d varlen=%d -> C=%lld S=%lld single=%d\n", batch, heads,
+                   (long long)L, d, B, (int)varlen, (long long)p.chunk, (long long)p.sub, (int)p.single_chunk);
+    }
+    printf("%ld plans, %ld bad\n", n, bad);
+    return bad != 0;
+}
