@@ -419,6 +419,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-extras", action="store_true", help="only the headline prefill workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode workload (one line with its figures; for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--workload", default="minimax_layer",
                     choices=["minimax_layer", "long_1m", "tiny_f32"],
@@ -439,6 +441,13 @@ def main():
 
     la.load_library()
     dev = torch.device("cuda:0")
+    if args.decode_only:
+        wd = synth.WORKLOADS["decode256"]
+        dms, dgbs, dtok = bench_decode(wd, 1, dev)
+        print(json.dumps({"decode": {"workload": wd.note, "ms_per_step": dms, "gbs": dgbs,
+                                     "hbm_frac": dgbs / PEAK_HBM_GBS, "head_steps_per_s": dtok}}),
+              flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     d, B = w.head_dim, w.block_size
     head_tokens = w.batch * w.heads * w.seq_len
