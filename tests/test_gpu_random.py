@@ -1,0 +1,127 @@
+"""Randomised parity: 120 seeded draws over the prefill's options at once
+(dtype, head dim, block size, dense or packed input with empty sequences,
+forced chunk and sub-chunk lengths, initial/final states or a pool with a
+slot table, the rotary prologue with position offsets), each against the CPU
+oracle.  Sizes stay small enough for the oracle's closed forms."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import TOL, chunk_tokens, device, host, note, randn_qkv
+
+pytestmark = pytest.mark.gpu
+
+STOL = {"bf16": 1e-4, "f32": 1e-4}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+def _draw(seed):
+    r = np.random.default_rng(1000 + seed)
+    c = {}
+    c["rope"] = bool(r.random() < 0.4)
+    c["dt"] = "bf16" if c["rope"] or r.random() < 0.6 else "f32"
+    c["d"] = int(r.choice([64, 128]))
+    c["B"] = int(r.choice([64, 128, 256]))
+    c["packed"] = bool(r.random() < 0.5)
+    nmax = 1200 if c["rope"] else 2500
+    if c["packed"]:
+        ns = int(r.integers(1, 7))
+        L = r.integers(0, nmax // 2, size=ns)
+        L[r.random(ns) < 0.2] = 0
+        if L.sum() == 0:
+            L[0] = 1
+        c["lengths"] = [int(x) for x in L]
+        c["heads"] = int(r.integers(1, 4))
+    else:
+        c["batch"], c["heads"] = int(r.integers(1, 4)), int(r.integers(1, 4))
+        c["n"] = int(r.integers(1, nmax))
+    if r.random() < 0.5:
+        c["C"] = c["B"] * int(r.choice([1, 2, 4, 8]))
+        c["S"] = c["C"] // int(r.choice([1, 2, 4])) if r.random() < 0.5 else 0
+        if c["S"] and c["S"] % c["B"]:
+            c["S"] = 0
+    else:
+        c["C"], c["S"] = 0, 0
+    c["state"] = str(r.choice(["none", "inout", "pool"] if c["packed"] else ["none", "inout"]))
+    c["base"] = float(r.choice([1e4, 1e7]))
+    c["seed"] = seed
+    return c
+
+
+@pytest.mark.parametrize("seed", range(120))
+def test_random_prefill(dev, seed):
+    import torch
+    import linear_attention_attn_amd as la
+    c = _draw(seed)
+    note(f"random {c}")
+    d, H = c["d"], c["heads"]
+    rng = np.random.default_rng(seed)
+    if c["packed"]:
+        cu = np.concatenate([[0], np.cumsum(c["lengths"])]).astype(np.int32)
+        T, nseq = int(cu[-1]), len(c["lengths"])
+        q, k, v = randn_qkv((H, T, d), c["dt"], 50 + seed, dev)
+        cud = torch.tensor(cu, device=dev)
+    else:
+        nseq = c["batch"]
+        q, k, v = randn_qkv((nseq, H, c["n"], d), c["dt"], 50 + seed, dev)
+        cud = None
+    off = rng.integers(0, 1 << 24, size=nseq).astype(np.int32) if c["rope"] else None
+    kw = {}
+    if c["rope"]:
+        kw = dict(rope_dims=d // 2, rope_base=c["base"], pos_offset=torch.tensor(off, device=dev))
+    S0 = None
+    pool = slots = None
+    if c["state"] == "inout":
+        S0 = torch.tensor(0.3 * rng.standard_normal((nseq, H, d, d)), dtype=torch.float32, device=dev)
+        Sf = torch.full_like(S0, float("nan"))
+        kw.update(s_init=S0, s_final=Sf)
+    elif c["state"] == "pool":
+        nslots = nseq + 2
+        pool = torch.tensor(0.3 * rng.standard_normal((nslots, H, d, d)), dtype=torch.float32, device=dev)
+        sl = rng.permutation(nslots)[:nseq].astype(np.int32)
+        sl[rng.random(nseq) < 0.25] = -1
+        slots = torch.tensor(sl, device=dev)
+        P0 = host(pool).astype(np.float64)
+        kw.update(state_pool=pool, slots=slots)
+    with chunk_tokens(c["C"], c["S"]):
+        o = host(la.fwd(q, k, v, block_size=c["B"], cu_seqlens=cud, **kw))
+        torch.cuda.synchronize()
+    # oracle
+    if c["state"] == "inout":
+        S0h = host(S0).astype(np.float64)
+    elif c["state"] == "pool":
+        S0h = np.zeros((nseq, H, d, d))
+        for s, x in enumerate(sl):
+            if x >= 0:
+                S0h[s] = P0[x]
+    else:
+        S0h = None
+    qh, kh, vh = host(q), host(k), host(v)
+    if c["rope"]:
+        if c["packed"]:
+            ref, sref = oracle.causal_linear_attention_rope_varlen(qh, kh, vh, cu, d // 2, c["base"], off, S0h)
+        else:
+            ref, sref = oracle.causal_linear_attention_rope(qh, kh, vh, d // 2, c["base"], off, S0h)
+        stol = TOL["bf16"]            # rotated keys enter the products rounded to bf16
+    else:
+        if c["packed"]:
+            ref, sref = oracle.causal_linear_attention_varlen_state(qh, kh, vh, cu, S0h)
+        else:
+            ref, sref = oracle.causal_linear_attention_state(qh, kh, vh, S0h)
+        stol = STOL[c["dt"]]
+    assert oracle.rel_err(o, ref) <= TOL[c["dt"]]
+    if c["state"] == "inout":
+        assert oracle.rel_err(host(kw["s_final"]), sref) <= stol
+    elif c["state"] == "pool":
+        P1 = host(pool)
+        for s, x in enumerate(sl):
+            if x >= 0:
+                assert oracle.rel_err(P1[x], sref[s]) <= stol, s
+        used = set(int(x) for x in sl if x >= 0)
+        for x in range(P1.shape[0]):
+            if x not in used:
+                assert np.array_equal(P1[x], P0[x].astype(np.float32)), x
