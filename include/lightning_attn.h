@@ -189,8 +189,9 @@ int lightning_attn_decode_indexed(const void *q, const void *k, const void *v, f
  *               state continues its positions).
  * q and k are read only (the rotation happens in registers and LDS).  The
  * final state is that of the rotated keys, the state a rotated decode step
- * (lightning_attn_decode_rope) continues.  dtype must be LA_DTYPE_BF16 (else
- * LA_EUNSUPPORTED).  Everything else is as lightning_attn_fwd_state.
+ * (lightning_attn_decode_rope) continues.  bf16 kernels rotate in fp32 and
+ * round the rotated values to bf16 for the matrix products; fp32 kernels keep
+ * them in fp32.  Everything else is as lightning_attn_fwd_state.
  */
 int lightning_attn_fwd_rope(const void *q, const void *k, const void *v, void *o,
                             int batch, int heads, int64_t seq_len, int head_dim, int block_size,
@@ -216,7 +217,7 @@ int lightning_attn_fwd_rope(const void *q, const void *k, const void *v, void *o
  *               sequences must not name the same slot (precondition, not
  *               checked).  A sequence of length 0 leaves its entry unchanged.
  *   rope_dims:  0 (no rotation) or head_dim / 2 with rope_base and pos_offset
- *               as in lightning_attn_fwd_rope (then dtype must be bf16).
+ *               as in lightning_attn_fwd_rope.
  * Everything else (layouts, cu_seqlens, workspace, checks) is as
  * lightning_attn_fwd.  Then o_i = q_i (S_slot + sum_{j <= i} k_j^T v_j).
  */

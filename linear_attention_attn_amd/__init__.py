@@ -213,7 +213,7 @@ def fwd(q, k, v, block_size: int = 256, cu_seqlens=None, out=None, workspace=Non
     (nseq = batch for dense input): the state each sequence starts from, and
     the tensor that receives each sequence's state after its last token (it
     may be s_init itself).
-    rope_dims > 0 (= d / 2, bf16 only): q and k rotated on the way in
+    rope_dims > 0 (= d / 2): q and k rotated on the way in
     (lightning_attn_fwd_rope), token t of sequence s at position
     pos_offset[s] + t (pos_offset: int32 device tensor [nseq], or None for 0).
     state_pool / slots: prefill over an indexed state table

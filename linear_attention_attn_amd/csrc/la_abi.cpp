@@ -189,7 +189,6 @@ static int fwd_common(const void *q, const void *k, const void *v, void *o, int 
                       const int32_t *slots = nullptr, int nslots = 0) {
     int st = la::check_fwd_shape(batch, heads, seq_len, head_dim, block_size, dtype);
     if (st != LA_OK) return st;
-    if (rope_dims != 0 && dtype != LA_DTYPE_BF16) return LA_EUNSUPPORTED;
     st = check_rope(rope_dims, rope_base, head_dim);
     if (st != LA_OK) return st;
     if (((uintptr_t)s_init & 15) != 0 || ((uintptr_t)s_final & 15) != 0) return LA_EINVAL;

@@ -402,6 +402,42 @@ __device__ __forceinline__ void patch_store(const Patch<T, D> &pt, char *kr, cha
     }
 }
 
+// Rotary embedding for the fp32 kernels.  Frequency in turns of pair i.
+__device__ __forceinline__ double rope_f_pair(const KParams &p, int i) {
+    return (0.5 / 3.14159265358979323846) * exp2(-2.0 * i / p.rope_dims * log2(p.rope_base));
+}
+
+// Rotate the K rows of a patch (the first NP threads hold 4 tokens x one
+// 16-byte chunk ch, dims 4 ch .. 4 ch + 3, of K; the partner chunk ch ^ HC,
+// HC = D / 16, sits in lane l ^ HC of the same wave).  pos0: position of
+// token 0 of the unit; tok0: the patch tile's first token.
+template <typename T, int D, int BLK>
+__device__ __forceinline__ void rope_patch(Patch<T, D> &pt, const KParams &p, int64_t pos0, int64_t tok0) {
+    using C = Cfg<T, D, BLK>;
+    static_assert(sizeof(T) == 4, "fp32 patches");
+    static_assert(C::NP % 64 == 0, "whole waves of K patch threads");
+    constexpr int HC = D / 16;
+    const int t = threadIdx.x;
+    if (t >= C::NP) return;                         // wave-uniform
+    const int tg = t / (D / C::EPC), ch = t % (D / C::EPC);
+    const bool rot = ch < 2 * HC, first = ch < HC;
+    const double f0 = rope_f_pair(p, 4 * (ch % HC)), rho = rope_rho(p.rope_base, p.rope_dims);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const double pos = (double)(pos0 + tok0 + 4 * tg + r);
+        double f = f0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x = __uint_as_float(pt.x[r][e]);
+            const float y = __uint_as_float((uint32_t)__shfl_xor((int)pt.x[r][e], HC));
+            float cs, sn;
+            rope_cs(pos, f, cs, sn);
+            f *= rho;
+            if (rot) pt.x[r][e] = __float_as_uint(first ? x * cs - y * sn : y * sn + x * cs);
+        }
+    }
+}
+
 // S[ia][ib] += K^T V over one LDS tile (TJ tokens).  Wave w owns the state
 // tiles a in [a0, a0+SA), b in [b0, b0+SB) (16 x 16 each).
 template <typename T, int D, int BLK, int SA, int SB>
@@ -428,7 +464,7 @@ __device__ __forceinline__ void state_update(f32x4_t (&S)[SA][SB], const char *k
 
 // --------------------------------------------------------- k_summary
 // states[h][sub-chunk] = K_c^T V_c  (fp32, row a = key dim, column b = value dim)
-template <typename T, int D, int BLK>
+template <typename T, int D, int BLK, bool ROPE>
 __global__ __launch_bounds__(512, 2) void k_summary(KParams p) {
     using C = Cfg<T, D, BLK>;
     __shared__ __attribute__((aligned(16))) char lds[2][2 * C::KT_BYTES];
@@ -452,13 +488,18 @@ __global__ __launch_bounds__(512, 2) void k_summary(KParams p) {
         for (int ib = 0; ib < C::SB; ++ib) S[ia][ib] = zero4();
 
     const int64_t ntile = (t1 - t0 + C::TJ - 1) / C::TJ;
+    const int64_t pos0 = ROPE && p.pos0 ? p.pos0[s] : 0;
     Patch<T, D> pt;
     patch_load<T, D, BLK>(pt, kb, vb, t0, t1);
+    if constexpr (ROPE) rope_patch<T, D, BLK>(pt, p, pos0, t0);
     patch_store<T, D, BLK, false>(pt, nullptr, lds[0], lds[0] + C::KT_BYTES);
     __syncthreads();
     for (int64_t it = 0; it < ntile; ++it) {
         const int buf = it & 1;
-        if (it + 1 < ntile) patch_load<T, D, BLK>(pt, kb, vb, t0 + (it + 1) * C::TJ, t1);
+        if (it + 1 < ntile) {
+            patch_load<T, D, BLK>(pt, kb, vb, t0 + (it + 1) * C::TJ, t1);
+            if constexpr (ROPE) rope_patch<T, D, BLK>(pt, p, pos0, t0 + (it + 1) * C::TJ);
+        }
         state_update<T, D, BLK, C::SA, C::SB>(S, lds[buf], lds[buf] + C::KT_BYTES, a0, b0);
         if (it + 1 < ntile)
             patch_store<T, D, BLK, false>(pt, nullptr, lds[buf ^ 1], lds[buf ^ 1] + C::KT_BYTES);
@@ -546,7 +587,7 @@ __device__ __forceinline__ void store_state(float *dst, const f32x4_t (&S)[SA][S
 }
 
 // ----------------------------------------------------------- k_fused
-template <typename T, int D, int BLK>
+template <typename T, int D, int BLK, bool ROPE>
 __global__ __launch_bounds__(512, 1) void k_fused(KParams p) {
     using C = Cfg<T, D, BLK>;
     constexpr int NBUF = (C::ES == 4 && D == 128) ? 1 : 2;
@@ -590,11 +631,15 @@ __global__ __launch_bounds__(512, 1) void k_fused(KParams p) {
     }
 
     const int64_t nblk = (t1 - t0 + BLK - 1) / BLK;
+    const int64_t pos0 = ROPE && p.pos0 ? p.pos0[s] : 0;
     Patch<T, D> pt;
     patch_load<T, D, BLK>(pt, kb, vb, t0, t1);
+    if constexpr (ROPE) rope_patch<T, D, BLK>(pt, p, pos0, t0);
     patch_store<T, D, BLK, true>(pt, lds, lds + C::KR_BYTES, lds + C::KR_BYTES + C::KT_BYTES);
 
     // Q fragments of this wave's row slabs: row 16*slab + c, d = 32*kc + 8g .. +7
+    // (with ROPE rotated once loaded: for d = 128 dims 8g + m of group 0 pair
+    // with group 1's in the same lane; for d = 64 with lane l ^ 32's)
     Frag<T> Q[C::NSW][C::KC];
     auto load_q = [&](int64_t tb) {
 #pragma unroll
@@ -604,6 +649,26 @@ __global__ __launch_bounds__(512, 1) void k_fused(KParams p) {
 #pragma unroll
             for (int kc = 0; kc < C::KC; ++kc)
                 Q[si][kc] = gload8<T>(qb + row * D + kc * 32 + 8 * g, ok);
+            if constexpr (ROPE) {
+                static_assert(sizeof(T) == 4, "fp32 fragments");
+                const double pos = (double)(pos0 + row), rho = rope_rho(p.rope_base, p.rope_dims);
+                double f = rope_f_pair(p, D == 128 ? 8 * g : 8 * (g & 1));
+#pragma unroll
+                for (int m = 0; m < 8; ++m) {
+                    float cs, sn;
+                    rope_cs(pos, f, cs, sn);
+                    f *= rho;
+                    if constexpr (D == 128) {
+                        const float x = Q[si][0].f[m], y = Q[si][1].f[m];
+                        Q[si][0].f[m] = x * cs - y * sn;
+                        Q[si][1].f[m] = x * sn + y * cs;
+                    } else {
+                        const float x = Q[si][0].f[m];
+                        const float y = __shfl_xor(x, 32);
+                        Q[si][0].f[m] = g < 2 ? x * cs - y * sn : y * sn + x * cs;
+                    }
+                }
+            }
         }
     };
     load_q(t0);
@@ -639,7 +704,10 @@ __global__ __launch_bounds__(512, 1) void k_fused(KParams p) {
             const bool last = jt + 1 == ntj;
             const bool nxt = !last || more;
             const int64_t ntok = last ? tb + BLK : tb + (jt + 1) * C::TJ;
-            if (nxt) patch_load<T, D, BLK>(pt, kb, vb, ntok, t1);
+            if (nxt) {
+                patch_load<T, D, BLK>(pt, kb, vb, ntok, t1);
+                if constexpr (ROPE) rope_patch<T, D, BLK>(pt, p, pos0, ntok);
+            }
 
             // ---- intra-block left product for this K/V tile
 #pragma unroll
@@ -1523,7 +1591,7 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
         if constexpr (sizeof(T) == 2)
             hipLaunchKernelGGL((k_summary_reg<D, BLK, 8, ROPE>), gsubs, dim3(512), 0, st, kp);
         else
-            hipLaunchKernelGGL((k_summary<T, D, BLK>), gsubs, dim3(512), 0, st, kp);
+            hipLaunchKernelGGL((k_summary<T, D, BLK, ROPE>), gsubs, dim3(512), 0, st, kp);
     }
     mark(2);
     if (!plan.single_chunk) {
@@ -1542,7 +1610,7 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
         hipLaunchKernelGGL((k_fused_dma<D, BLK, NWF, 64, 4, 2, ROPE>), gchunks, dim3(NWF * 64), 0, st, kp);
     }
     else
-        hipLaunchKernelGGL((k_fused<T, D, BLK>), gchunks, dim3(512), 0, st, kp);
+        hipLaunchKernelGGL((k_fused<T, D, BLK, ROPE>), gchunks, dim3(512), 0, st, kp);
     mark(4);
     return hipGetLastError();
 }
@@ -1603,9 +1671,13 @@ int launch_fwd(const FwdArgs &a, void *stream, void *const *events) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (a.rope_dims > 0) {
-        // bf16 only, rope_dims == head_dim / 2 (checked by the caller)
-        e = a.head_dim == 64 ? launch_blk<bf16_t, 64, true>(kp, a.plan, a.block_size, st, events)
-                             : launch_blk<bf16_t, 128, true>(kp, a.plan, a.block_size, st, events);
+        // rope_dims == head_dim / 2 (checked by the caller)
+        if (a.dtype == 0)
+            e = a.head_dim == 64 ? launch_blk<bf16_t, 64, true>(kp, a.plan, a.block_size, st, events)
+                                 : launch_blk<bf16_t, 128, true>(kp, a.plan, a.block_size, st, events);
+        else
+            e = a.head_dim == 64 ? launch_blk<float, 64, true>(kp, a.plan, a.block_size, st, events)
+                                 : launch_blk<float, 128, true>(kp, a.plan, a.block_size, st, events);
     } else if (a.dtype == 0) {
         e = a.head_dim == 64 ? launch_blk<bf16_t, 64>(kp, a.plan, a.block_size, st, events)
                              : launch_blk<bf16_t, 128>(kp, a.plan, a.block_size, st, events);

@@ -111,7 +111,7 @@ def test_rope_rejects(la):
     def fr(d, dt, r, base):
         return la.lightning_attn_fwd_rope(fake, fake, fake, fake, 1, 1, 10, d, 64, None, dt, r, base,
                                           None, None, None, fake, need, None)
-    assert fr(128, 1, 64, 1e4) == 2          # fp32 input: unsupported with rotation
+    assert fr(128, 3, 64, 1e4) == 2          # unknown dtype
     assert fr(128, 0, 32, 1e4) == 2          # only half the head dims
     assert fr(128, 0, 128, 1e4) == 2
     assert fr(128, 0, 0, 1e4) == 2           # the rotary entry point needs rope_dims > 0
@@ -143,7 +143,7 @@ def test_fwd_indexed_rejects(la):
     assert fi(slots=None) == 1               # the slot table is required
     assert fi(nslots=-1) == 1
     assert fi(pool=None) == 1                # a pool is needed when it has entries
-    assert fi(dt=1, r=64) == 2               # rotation: bf16 only
+    assert fi(dt=3, r=64) == 2               # unknown dtype
     assert fi(r=32) == 2                     # rotation: half the head dims only
     assert fi(r=64, base=0.0) == 1
     assert fi(pool=fake + 4) == 1            # 16-byte alignment

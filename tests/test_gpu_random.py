@@ -23,7 +23,7 @@ def _draw(seed):
     r = np.random.default_rng(1000 + seed)
     c = {}
     c["rope"] = bool(r.random() < 0.4)
-    c["dt"] = "bf16" if c["rope"] or r.random() < 0.6 else "f32"
+    c["dt"] = "bf16" if r.random() < 0.6 else "f32"
     c["d"] = int(r.choice([64, 128]))
     c["B"] = int(r.choice([64, 128, 256]))
     c["packed"] = bool(r.random() < 0.5)
@@ -106,7 +106,8 @@ def test_random_prefill(dev, seed):
             ref, sref = oracle.causal_linear_attention_rope_varlen(qh, kh, vh, cu, d // 2, c["base"], off, S0h)
         else:
             ref, sref = oracle.causal_linear_attention_rope(qh, kh, vh, d // 2, c["base"], off, S0h)
-        stol = TOL["bf16"]            # rotated keys enter the products rounded to bf16
+        # bf16: the rotated keys enter the products rounded to bf16
+        stol = TOL["bf16"] if c["dt"] == "bf16" else STOL["f32"]
     else:
         if c["packed"]:
             ref, sref = oracle.causal_linear_attention_varlen_state(qh, kh, vh, cu, S0h)

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 # bf16 (the operand type), a relative error of up to 2^-9 per key element
 # that the fp32 state sums carry (measured ~7e-4 of max|S|), so they are held
 # to the bf16 bar; the plain path's states see exact bf16 inputs instead.
-# Decode rotates in fp32 and keeps the plain path's fp32 state bar.
+# Decode and the fp32 prefill rotate in fp32 and keep the fp32 state bar.
 RSTOL = TOL["bf16"]
 STOL = 1e-4
 
@@ -48,13 +48,14 @@ for d in (64, 128):
 
 @pytest.mark.parametrize("d,B,n,C,S", CASES)
 @pytest.mark.parametrize("base", [1e4, 1e7])
-def test_rope_prefill_dense(dev, d, B, n, C, S, base):
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_rope_prefill_dense(dev, dt, d, B, n, C, S, base):
     """Dense input, zero and nonzero position offsets, initial and final
     states; one chunk, many chunks, chunks of several summary sub-chunks."""
     import torch
     import linear_attention_attn_amd as la
-    note(f"rope dense d={d} B={B} n={n} C={C} S={S} base={base}")
-    q, k, v = randn_qkv((2, 3, n, d), "bf16", 7000 + n + d + B, dev)
+    note(f"rope dense dt={dt} d={d} B={B} n={n} C={C} S={S} base={base}")
+    q, k, v = randn_qkv((2, 3, n, d), dt, 7000 + n + d + B, dev)
     off = [0, 123457]
     S0 = _states((2, 3, d, d), 71 + d, dev)
     Sf = torch.empty_like(S0)
@@ -64,8 +65,8 @@ def test_rope_prefill_dense(dev, d, B, n, C, S, base):
         torch.cuda.synchronize()
     ref, sref = oracle.causal_linear_attention_rope(host(q), host(k), host(v), d // 2, base, off,
                                                     host(S0))
-    assert oracle.rel_err(host(o), ref) <= TOL["bf16"]
-    assert oracle.rel_err(host(Sf), sref) <= RSTOL
+    assert oracle.rel_err(host(o), ref) <= TOL[dt]
+    assert oracle.rel_err(host(Sf), sref) <= (RSTOL if dt == "bf16" else STOL)
 
 
 @pytest.mark.parametrize("C", [0, 256])
@@ -87,15 +88,16 @@ def test_rope_without_state_or_offset(dev, C):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_rope_packed(dev, d):
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_rope_packed(dev, dt, d):
     """Packed sequences (some empty) restart positions at their offsets."""
     import torch
     import linear_attention_attn_amd as la
     lengths = (5, 0, 700, 1, 1300, 0, 257)
-    note(f"rope packed d={d} lengths={lengths}")
+    note(f"rope packed dt={dt} d={d} lengths={lengths}")
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     T, H = int(cu[-1]), 3
-    q, k, v = randn_qkv((H, T, d), "bf16", 4545 + d, dev)
+    q, k, v = randn_qkv((H, T, d), dt, 4545 + d, dev)
     off = [3, 0, 1 << 20, 7, 65536, 11, 999999]
     S0 = _states((len(lengths), H, d, d), 4646, dev)
     Sf = torch.full_like(S0, float("nan"))
@@ -105,8 +107,8 @@ def test_rope_packed(dev, d):
         torch.cuda.synchronize()
     ref, sref = oracle.causal_linear_attention_rope_varlen(host(q), host(k), host(v), cu, d // 2,
                                                            1e7, off, host(S0))
-    assert oracle.rel_err(host(o), ref) <= TOL["bf16"]
-    assert oracle.rel_err(host(Sf), sref) <= RSTOL
+    assert oracle.rel_err(host(o), ref) <= TOL[dt]
+    assert oracle.rel_err(host(Sf), sref) <= (RSTOL if dt == "bf16" else STOL)
     for s, L in enumerate(lengths):
         if L == 0:
             assert np.array_equal(host(Sf)[s], host(S0)[s])
