@@ -84,6 +84,8 @@ int64_t lightning_attn_fwd_chunk_tokens(int batch, int heads, int64_t seq_len, i
  * workspace: device memory of at least lightning_attn_fwd_workspace_size(...)
  * bytes (same arguments, varlen = cu_seqlens != NULL), 256-byte aligned.
  *
+ * q, k, v, o and the workspace must be 16-byte aligned and cu_seqlens 4-byte
+ * aligned (else LA_EINVAL; the kernels move 16-byte vectors).
  * All argument checks happen on the host before any launch; a rejected call
  * writes nothing.  seq_len == 0 returns LA_OK without touching any pointer.
  * Device-side faults surface at the caller's next synchronisation.
@@ -148,7 +150,8 @@ int lightning_attn_fwd_traced(const void *q, const void *k, const void *v, void 
  *               a = key dimension, b = value dimension; read and updated in
  *               place (caller-owned: a checkpoint is a copy of it).
  *   o = q . state_old ;  state_new = state_old + k^T v .
- * o must not alias the other buffers.  Checks happen on the host first.
+ * o must not alias the other buffers; state must be 16-byte aligned (else
+ * LA_EINVAL).  Checks happen on the host first.
  */
 int lightning_attn_decode(const void *q, const void *k, const void *v, float *state, void *o,
                           int batch, int heads, int head_dim, int dtype, void *stream);

@@ -29,6 +29,11 @@ int check_fwd_shape(int batch, int heads, int64_t seq_len, int head_dim, int blo
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The kernels move q, k, v, o and states in 16-byte vectors.
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+// int32 tables (cu_seqlens, slots, positions, offsets).
+static bool aligned4(const void *p) { return ((uintptr_t)p & 3) == 0; }
+
 static int64_t env_i64(const char *name, int64_t dflt) {
     const char *s = getenv(name);
     if (!s || !*s) return dflt;
@@ -199,6 +204,8 @@ static int fwd_common(const void *q, const void *k, const void *v, void *o, int 
         return la::launch_state_empty(s_init, s_final, batch, heads, head_dim, stream) == 0 ? LA_OK : LA_EHIP;
     }
     if (!q || !k || !v || !o) return LA_EINVAL;
+    if (!la::aligned16(q) || !la::aligned16(k) || !la::aligned16(v) || !la::aligned16(o)) return LA_EINVAL;
+    if (!la::aligned4(cu_seqlens) || !la::aligned4(pos0) || !la::aligned4(slots)) return LA_EINVAL;
     la::FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o;
     a.nseq = batch; a.heads = heads; a.head_dim = head_dim; a.block_size = block_size;
@@ -272,6 +279,7 @@ int lightning_attn_decode(const void *q, const void *k, const void *v, float *st
     if (batch < 1 || heads < 1) return LA_EINVAL;
     if ((int64_t)batch * heads > (int64_t)INT32_MAX) return LA_EUNSUPPORTED;
     if (!q || !k || !v || !state || !o) return LA_EINVAL;
+    if (!la::aligned16(state)) return LA_EINVAL;
     return la::launch_decode(q, k, v, state, o, batch, heads, head_dim, dtype, stream) == 0 ? LA_OK : LA_EHIP;
 }
 
@@ -284,6 +292,7 @@ int lightning_attn_decode_indexed(const void *q, const void *k, const void *v, f
     if ((int64_t)batch * heads > (int64_t)INT32_MAX || (int64_t)nslots * heads > (int64_t)INT32_MAX)
         return LA_EUNSUPPORTED;
     if (!q || !k || !v || !slots || !o || (nslots > 0 && !state_pool)) return LA_EINVAL;
+    if (!la::aligned16(state_pool) || !la::aligned4(slots)) return LA_EINVAL;
     return la::launch_decode(q, k, v, state_pool, o, batch, heads, head_dim, dtype, stream, slots,
                              nslots) == 0 ? LA_OK : LA_EHIP;
 }
@@ -300,6 +309,7 @@ int lightning_attn_decode_rope(const void *q, const void *k, const void *v, floa
     if (batch < 1 || heads < 1) return LA_EINVAL;
     if ((int64_t)batch * heads > (int64_t)INT32_MAX) return LA_EUNSUPPORTED;
     if (!q || !k || !v || !o || !positions) return LA_EINVAL;
+    if (!la::aligned16(state) || !la::aligned4(positions) || !la::aligned4(slots)) return LA_EINVAL;
     if (slots) {
         if (nslots < 0) return LA_EINVAL;
         if ((int64_t)nslots * heads > (int64_t)INT32_MAX) return LA_EUNSUPPORTED;

@@ -95,6 +95,24 @@ def test_fwd_null_pointers_and_workspace(la):
     assert la.lightning_attn_fwd(fake, fake, fake, fake, 1, 1, 10, 64, 64, None, 0, fake + 8, need, None) == 1
 
 
+def test_misaligned_pointers_rejected(la):
+    """The kernels move 16-byte vectors: misaligned buffers are rejected on
+    the host (never launched)."""
+    fake = 1 << 20
+    need = la.lightning_attn_fwd_workspace_size(1, 1, 10, 64, 64, 0, 0)
+    for i in range(4):
+        ptrs = [fake] * 4
+        ptrs[i] = fake + 2
+        assert la.lightning_attn_fwd(*ptrs, 1, 1, 10, 64, 64, None, 0, fake, need, None) == 1, i
+    assert la.lightning_attn_fwd(fake, fake, fake, fake, 1, 1, 10, 64, 64, fake + 2, 0, fake, need, None) == 1
+    assert la.lightning_attn_decode(fake, fake, fake, fake + 4, fake, 1, 1, 64, 0, None) == 1
+    assert la.lightning_attn_decode_indexed(fake, fake, fake, fake + 8, 1, fake, fake, 1, 1, 64, 0, None) == 1
+    assert la.lightning_attn_decode_rope(fake, fake, fake, fake + 4, 0, None, fake, 1, 1, 128, 0, 64, 1e4,
+                                         fake, None) == 1
+    assert la.lightning_attn_decode_rope(fake, fake, fake, fake, 0, None, fake, 1, 1, 128, 0, 64, 1e4,
+                                         fake + 1, None) == 1
+
+
 def test_decode_rejects(la):
     fake = 1 << 20
     assert la.lightning_attn_decode(fake, fake, fake, fake, fake, 1, 1, 96, 0, None) == 2
