@@ -76,7 +76,10 @@ int64_t lightning_attn_fwd_chunk_tokens(int batch, int heads, int64_t seq_len, i
  *   cu_seqlens is a DEVICE int32 array of batch+1 entries with
  *   cu_seqlens[0] = 0, non-decreasing, cu_seqlens[batch] = T.  Sequence s is
  *   tokens [cu_seqlens[s], cu_seqlens[s+1]) of every head and starts from an
- *   empty state.  These contents are a precondition, not checked.
+ *   empty state.  The device checks these contents before any other work: a
+ *   malformed table makes the call compute nothing (o is left as it was);
+ *   with the environment variable LA_DEBUG_CHECKS=1 the call also waits for
+ *   the stream and returns LA_EINVAL in that case.
  *
  * block_size in {64, 128, 256}; head_dim in {64, 128}; blocks start at each
  * sequence's first token and the last block of a sequence may be short.

@@ -141,6 +141,8 @@ void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int bloc
     p.off_sub_off = off;
     off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));
     if (varlen) {
+        p.off_err = off;
+        off = align256(off + sizeof(int32_t));
         p.off_perm = off;
         off = align256(off + (size_t)batch * sizeof(int32_t));
         p.off_rank_off = off;
@@ -217,7 +219,13 @@ static int fwd_common(const void *q, const void *k, const void *v, void *o, int 
     if (!workspace || workspace_bytes < a.plan.bytes) return LA_EWORKSPACE;
     if (((uintptr_t)workspace & 255) != 0) return LA_EINVAL;
     a.workspace = static_cast<char *>(workspace);
-    return la::launch_fwd(a, stream, events) == 0 ? LA_OK : LA_EHIP;
+    if (la::launch_fwd(a, stream, events) != 0) return LA_EHIP;
+    if (cu_seqlens && la::env_i64("LA_DEBUG_CHECKS", 0) > 0) {
+        int bad = 0;
+        if (la::read_cu_error(a, stream, &bad) != 0) return LA_EHIP;
+        if (bad) return LA_EINVAL;
+    }
+    return LA_OK;
 }
 
 int lightning_attn_fwd(const void *q, const void *k, const void *v, void *o, int batch, int heads,

@@ -24,6 +24,7 @@ struct FwdPlan {
     bool single_chunk = false;  // every sequence is one chunk: no summaries, no scan
     size_t off_chunk_off = 0; // int32 [nseq + 1]
     size_t off_sub_off = 0;   // int32 [nseq + 1]
+    size_t off_err = 0;       // int32: 1 when cu_seqlens was found malformed (packed input)
     size_t off_perm = 0;      // int32 [nseq] (packed input: sequences longest first)
     size_t off_rank_off = 0;  // int32 [nseq + 1]
     size_t off_tile_off = 0;  // int32 [nseq + 1]
@@ -62,6 +63,10 @@ struct FwdArgs {
 // non-null it holds 5 hipEvent_t handles recorded at the stage boundaries.
 // Returns 0 or a HIP error code.
 int launch_fwd(const FwdArgs &a, void *stream, void *const *events);
+
+// Wait for `stream` and read the flag k_prep raises for a malformed
+// cu_seqlens (packed input).  Returns 0 or a HIP error code.
+int read_cu_error(const FwdArgs &a, void *stream, int *flag);
 
 // Queue the kernel that sets the final state of every sequence of length 0
 // (all of them when there are no tokens at all) to its initial state.

@@ -45,6 +45,7 @@ struct KParams {
     int32_t *rank_off;      // [nseq + 1]
     int32_t *sub_off;       // [nseq + 1] sub-chunks before each sequence
     int32_t *tile_off;      // [nseq + 1] scan tiles before each sequence
+    int32_t *err;           // set to 1 by k_prep when cu_seqlens is malformed
     float *states;          // [heads][nsub_ub][D*D]
     float *tilesum;         // [heads][ntile_ub][D*D]
     int64_t seq_len;        // dense: per sequence; packed: total tokens
@@ -188,6 +189,28 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(KParams p) {
     const int t = threadIdx.x;
     const int per = (p.nseq + kPrepThreads - 1) / kPrepThreads;
     const int s0 = t * per, s1 = min(p.nseq, s0 + per);
+    // cu_seqlens must start at 0, never decrease and end at the token count.
+    // A malformed table must not send any kernel out of bounds: every
+    // sequence is then given no chunks (nothing is computed) and the error
+    // flag is raised.
+    if (p.cu != nullptr) {
+        int bad = 0;
+        for (int s = s0; s < s1; ++s) bad |= p.cu[s + 1] < p.cu[s];
+        if (t == 0) bad |= p.cu[0] != 0 || (int64_t)p.cu[p.nseq] != p.seq_len;
+        if (__syncthreads_or(bad)) {
+            for (int s = s0; s < s1; ++s) {
+                p.chunk_off[s] = 0; p.sub_off[s] = 0; p.tile_off[s] = 0;
+                if (p.perm) { p.perm[s] = s; p.rank_off[s] = 0; }
+            }
+            if (t == 0) {
+                p.chunk_off[p.nseq] = 0; p.sub_off[p.nseq] = 0; p.tile_off[p.nseq] = 0;
+                if (p.rank_off) p.rank_off[p.nseq] = 0;
+                if (p.err) p.err[0] = 1;
+            }
+            return;
+        }
+        if (t == 0 && p.err) p.err[0] = 0;
+    }
     auto counts = [&](int s, int64_t &nc, int64_t &ns, int64_t &ng) {
         const int64_t L = p.cu ? (int64_t)p.cu[s + 1] - p.cu[s] : p.seq_len;
         nc = (L + p.chunk - 1) / p.chunk;
@@ -1625,6 +1648,15 @@ static hipError_t launch_blk(const KParams &kp, const FwdPlan &plan, int blk, hi
     }
 }
 
+int read_cu_error(const FwdArgs &a, void *stream, int *flag) {
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    int32_t h = 0;
+    hipError_t e = hipMemcpyAsync(&h, a.workspace + a.plan.off_err, sizeof(h), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    *flag = h;
+    return (int)e;
+}
+
 int launch_state_empty(const float *s_init, float *s_final, int nseq, int heads, int head_dim,
                        void *stream) {
     KParams kp{};
@@ -1649,6 +1681,7 @@ int launch_fwd(const FwdArgs &a, void *stream, void *const *events) {
     kp.perm = a.cu_seqlens ? reinterpret_cast<int32_t *>(a.workspace + a.plan.off_perm) : nullptr;
     kp.rank_off = a.cu_seqlens ? reinterpret_cast<int32_t *>(a.workspace + a.plan.off_rank_off) : nullptr;
     kp.tile_off = reinterpret_cast<int32_t *>(a.workspace + a.plan.off_tile_off);
+    kp.err = a.cu_seqlens ? reinterpret_cast<int32_t *>(a.workspace + a.plan.off_err) : nullptr;
     kp.states = reinterpret_cast<float *>(a.workspace + a.plan.off_states);
     kp.tilesum = reinterpret_cast<float *>(a.workspace + a.plan.off_tilesum);
     kp.seq_len = a.seq_len;

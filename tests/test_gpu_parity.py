@@ -152,6 +152,38 @@ def test_varlen_many_sequences(dev, nseq):
     assert oracle.rel_err(o, ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("cu_h", [[0, 100, 50, 200], [0, 100, 150, 300], [5, 100, 150, 200]])
+def test_varlen_malformed_cu_seqlens(dev, cu_h):
+    """A decreasing table, one not ending at the token count, one not
+    starting at 0: the device check makes the call compute nothing (o keeps
+    its contents, nothing is read or written out of bounds), and with
+    LA_DEBUG_CHECKS=1 the call reports LA_EINVAL."""
+    import os
+    import torch
+    import linear_attention_attn_amd as la
+    note(f"varlen malformed cu={cu_h}")
+    T, H, d = 200, 2, 128
+    q, k, v = randn_qkv((H, T, d), "bf16", 3, dev)
+    cud = torch.tensor(cu_h, dtype=torch.int32, device=dev)
+    o = torch.full_like(q, float("nan"))
+    la.fwd(q, k, v, 64, cud, out=o)
+    torch.cuda.synchronize()
+    assert np.isnan(host(o)).all()
+    os.environ["LA_DEBUG_CHECKS"] = "1"
+    try:
+        with pytest.raises(la.LightningAttnError) as ei:
+            la.fwd(q, k, v, 64, cud, out=o)
+        assert ei.value.status == la.LA_EINVAL
+        good = torch.tensor([0, 100, 150, 200], dtype=torch.int32, device=dev)
+        o2 = la.fwd(q, k, v, 64, good)                 # a valid table passes the check
+        torch.cuda.synchronize()
+        ref = oracle.causal_linear_attention_varlen(host(q), host(k), host(v),
+                                                    np.array([0, 100, 150, 200]), "recurrent")
+        assert oracle.rel_err(host(o2), ref) <= TOL["bf16"]
+    finally:
+        os.environ.pop("LA_DEBUG_CHECKS", None)
+
+
 def test_varlen_equals_separate_runs(dev):
     import torch
     lengths = (700, 1, 2500, 256, 0, 1300)
