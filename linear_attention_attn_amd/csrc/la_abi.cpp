@@ -133,6 +133,7 @@ void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int bloc
         p.nsub_ub = seq_len / Cs + batch;
         p.ntile_ub = (p.nsub_ub + G - 1) / G + batch;
         p.scan_tiles = cdiv(seq_len, Cs) > G;
+        p.single_chunk = seq_len <= C;   // no sequence is longer than the whole input
     }
     const size_t dd = (size_t)head_dim * head_dim * sizeof(float);
     size_t off = 0;

@@ -55,8 +55,9 @@ struct KParams {
     int nseq, heads, group;
     // state handoff: initial states [nseq][heads][D][D] (or nullptr = zero)
     // and final states of the same layout (or nullptr = not wanted).
-    // init_mode 0: no initial state; 1: the scan adds it to every sub-chunk's
-    // prefix in `states`; 2: one chunk per sequence, read directly.
+    // init_mode 0: no initial state; 1: the scan adds it to the prefixes in
+    // `states` of sequences of several chunks, and a sequence of one chunk
+    // reads it directly; 2: every sequence is one chunk and reads it directly.
     // With a slot table, s_init and s_final are one pool of nslots entries
     // and sequence s uses entry slots[s] (none when out of range).
     const float *s_init;
@@ -137,11 +138,14 @@ __device__ __forceinline__ int64_t state_entry(const KParams &p, int s) {
 // Source of the state at the start of chunk cl (chunk-local index) of
 // sequence s, head h, or nullptr for zero: the scanned prefix in `states` at
 // the chunk's first sub-chunk (which includes a carried-in initial state when
-// one was given), or with one chunk per sequence the initial state itself.
+// one was given), or for a sequence of one chunk the initial state itself
+// (read and then overwritten by the same workgroup, so an initial state that
+// is also the final state's memory is safe; with several chunks the scan
+// copies it first, since the last chunk's workgroup writes the final state).
 template <int D>
 __device__ __forceinline__ const float *chunk_start_state(const KParams &p, int s, int h, int64_t cl) {
-    if (p.init_mode == 2) {
-        const int64_t e = state_entry(p, s);
+    if (p.init_mode == 2 || p.chunk_off[s + 1] - p.chunk_off[s] == 1) {
+        const int64_t e = p.init_mode == 0 ? -1 : state_entry(p, s);
         return e < 0 ? nullptr : p.s_init + (e * p.heads + h) * (D * D);
     }
     if (p.init_mode == 0 && cl == 0) return nullptr;
@@ -179,8 +183,11 @@ __global__ __launch_bounds__(256) void k_state_empty(KParams p) {
 }
 
 // -------------------------------------------------------------- k_prep
-// chunk_off[s] = sum_{s' < s} ceil(L_s' / C), sub_off[s] = sum ceil(L_s' / C_s),
-// tile_off[s] = sum ceil(ns_s' / G) (ns = sub-chunks of a sequence).
+// chunk_off[s] = sum_{s' < s} nc_s', nc = ceil(L / C) chunks of a sequence;
+// sub_off[s] = sum ns_s', where ns = (nc - 1) C / C_s + 1 sub-chunk entries
+// when nc >= 2 (the summaries of every chunk but the last, and one entry for
+// the last chunk's start prefix) and 0 for a sequence of one chunk, which
+// needs no prefix; tile_off[s] = sum ceil(ns_s' / G).
 constexpr int kPrepThreads = 1024;
 constexpr int kSortMax = 4096;   // sequences ranked by length for the fused grid
 
@@ -214,7 +221,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(KParams p) {
     auto counts = [&](int s, int64_t &nc, int64_t &ns, int64_t &ng) {
         const int64_t L = p.cu ? (int64_t)p.cu[s + 1] - p.cu[s] : p.seq_len;
         nc = (L + p.chunk - 1) / p.chunk;
-        ns = (L + p.sub - 1) / p.sub;
+        ns = nc >= 2 ? (nc - 1) * (p.chunk / p.sub) + 1 : 0;
         ng = (ns + p.group - 1) / p.group;
     };
     int64_t c = 0, u = 0, g = 0;
@@ -543,8 +550,10 @@ __global__ __launch_bounds__(512, 2) void k_summary(KParams p) {
 // on `states`.  Lanes are the d*d state entries; tiles of G sub-chunks are
 // reduced (A), the tile totals scanned per sequence (B), and each tile
 // rescanned from its prefix (C).  With every sequence inside one tile only
-// phase C runs.  (Entries of sub-chunks in a sequence's last chunk hold no
-// summary; they only reach prefixes that are never read.)
+// phase C runs.  Only chunk starts are read back, so C writes the prefix
+// there and nowhere else.  (A sequence's last entry, the last chunk's start,
+// holds no summary; it only reaches the tile total of the last tile, which
+// no prefix uses.)
 constexpr int kScanThreads = 256;
 
 template <int D>
@@ -590,10 +599,13 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_apply(KParams p, int use_
         const int64_t se = state_entry(p, s);
         if (se >= 0) run += p.s_init[(se * p.heads + h) * (D * D) + e];
     }
+    const int64_t per = p.chunk / p.sub;
+    int64_t j = (c0 - p.sub_off[s]) % per;            // sub-chunk index within its chunk
     for (int64_t c = c0; c < c1; ++c) {
         const float x = st[c * (D * D)];
-        st[c * (D * D)] = run;
+        if (j == 0) st[c * (D * D)] = run;
         run += x;
+        if (++j == per) j = 0;
     }
 }
 
