@@ -1368,8 +1368,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     issue(0, stages[0]);
     if constexpr (LA >= 3) issue(1, stages[1]);
     float *const fdst = final_state_dst<D>(p, s, h, gch);
+    const float *const src = chunk_start_state<D>(p, s, h, cl);
+    const bool zs = src == nullptr;
     {
-        const float *src = chunk_start_state<D>(p, s, h, cl);
 #pragma unroll
         for (int ia = 0; ia < C::SA; ++ia)
 #pragma unroll
@@ -1433,7 +1434,15 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         const char *krow = stage + row8;             // K rows (b128 reads)
         const char *vcol = stage + vpv_off;          // V columns of tile ct0 (tr reads)
 
-        if constexpr (first) {
+        // a chunk that starts from zero has Q S = 0 in its first block
+        bool zero_s = false;
+        if constexpr (first && J < TPB) zero_s = zs && sb == 0;
+        if (zero_s) {
+#pragma unroll
+            for (int si = 0; si < C::NSW; ++si)
+#pragma unroll
+                for (int ct = 0; ct < C::NCT; ++ct) O[si][ct] = zero4();
+        } else if constexpr (first) {
             // ---- inter-block right product with the block-start state
             const char *srow = st + row8 + ct0 * 16 * 64;
 #pragma unroll
