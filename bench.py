@@ -155,7 +155,7 @@ def bench_prefill_varlen(w, steps, warmup, dev):
     import linear_attention_attn_amd as la
     import synth
 
-    lengths = synth.varlen_lengths(w.batch, w.len_seed)
+    lengths = synth.varlen_lengths(w.batch, w.len_seed, w.len_lo, w.len_hi)
     q, k, v, cu = synth.varlen_inputs(lengths, w.heads, w.head_dim, w.dtype, w.cid, dev)
     T = int(cu[-1])
     cud = torch.tensor(cu, dtype=torch.int32, device=dev)
@@ -533,20 +533,21 @@ def main():
                           "kernels_ms": lstage, "chunk_tokens": lchunk}
         out["long_1m"]["mfma_frac"] = out["long_1m"]["tflops"] / PEAK_BF16_TFLOPS
         log(json.dumps(out["long_1m"]))
-        wv = synth.WORKLOADS["varlen16"]
-        log(f"prefill {wv.name}: {wv.note}")
-        vms, vstage, vchunk, vT = bench_prefill_varlen(wv, 10, 5, dev)
-        vht = wv.heads * vT
-        vbytes = vht * 4 * wv.head_dim * 2
-        out["varlen16"] = {"workload": f"{wv.note}, H{wv.heads} d{wv.head_dim}, block {wv.block_size}, "
-                                       f"{vT} tokens",
-                           "ms_per_step": vms, "tokens_per_s": vT / (vms * 1e-3),
-                           "tflops": vht * prefill_flops_per_head_token(wv.head_dim, wv.block_size)
-                           / (vms * 1e-3) / 1e12,
-                           "hbm_gbs": vbytes / (vms * 1e-3) / 1e9,
-                           "roofline_frac": vbytes / (PEAK_HBM_GBS * 1e9) / (vms * 1e-3),
-                           "kernels_ms": vstage, "chunk_tokens": vchunk}
-        log(json.dumps(out["varlen16"]))
+        for vname, vsteps in (("varlen16", 10), ("varlen_short", 50)):
+            wv = synth.WORKLOADS[vname]
+            log(f"prefill {wv.name}: {wv.note}")
+            vms, vstage, vchunk, vT = bench_prefill_varlen(wv, vsteps, 5, dev)
+            vht = wv.heads * vT
+            vbytes = vht * 4 * wv.head_dim * 2
+            out[vname] = {"workload": f"{wv.note}, H{wv.heads} d{wv.head_dim}, block {wv.block_size}, "
+                                      f"{vT} tokens",
+                          "ms_per_step": vms, "tokens_per_s": vT / (vms * 1e-3),
+                          "tflops": vht * prefill_flops_per_head_token(wv.head_dim, wv.block_size)
+                          / (vms * 1e-3) / 1e12,
+                          "hbm_gbs": vbytes / (vms * 1e-3) / 1e9,
+                          "roofline_frac": vbytes / (PEAK_HBM_GBS * 1e9) / (vms * 1e-3),
+                          "kernels_ms": vstage, "chunk_tokens": vchunk}
+            log(json.dumps(out[vname]))
 
     if args.copy_calibration:
         out["copy_calibration"] = copy_calibration(dev)

@@ -130,8 +130,10 @@ void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int bloc
         p.single_chunk = cps == 1;
     } else {
         p.nchunk_ub = seq_len / C + batch;
-        p.nsub_ub = seq_len / Cs + batch;
-        p.ntile_ub = (p.nsub_ub + G - 1) / G + batch;
+        // Only a sequence longer than C has sub-chunk entries, (nc - 1) C / Cs + 1
+        // < L / Cs + 1 of them, and there are at most T / C such sequences.
+        p.nsub_ub = seq_len / Cs + seq_len / C;
+        p.ntile_ub = p.nsub_ub / G + 1 + seq_len / C;
         p.scan_tiles = cdiv(seq_len, Cs) > G;
         p.single_chunk = seq_len <= C;   // no sequence is longer than the whole input
     }

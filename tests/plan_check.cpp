@@ -2,11 +2,16 @@
 // random shapes: chunk and sub-chunk lengths are multiples of the block size,
 // the chunk a multiple of the sub-chunk, sub-chunks at most 16384 tokens
 // (unless one chunk covers the sequence), chunk rows within 2^30 bytes, and the
-// slot counts match the dense shape.  Built with g++ against stubs of the
-// launchers; run by tests/test_plan_host.py.
+// slot counts match the dense shape; for packed input, over random and
+// adversarial splits of the tokens into sequences, the chunk, sub-chunk and
+// scan-tile counts the device derives from the lengths stay within the plan's
+// bounds.  Built with g++ against stubs of the launchers; run by
+// tests/test_plan_host.py.
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <random>
+#include <vector>
 #include "la_internal.h"
 namespace la {
 int launch_fwd(const FwdArgs &, void *, void *const *) { return 0; }
@@ -34,6 +39,37 @@ int main() {  // exit status 0 when every plan passes
         if (!varlen) {
             const int64_t cps = (L + p.chunk - 1) / p.chunk;
             ok = ok && p.nchunk_ub == batch * cps && p.single_chunk == (cps == 1);
+        } else {
+            // split L tokens into batch sequences: random cuts, or as many
+            // sequences of C + 1 tokens as fit (the most sequences of two
+            // chunks), or of 1 token (the most sequences)
+            std::vector<int64_t> len(batch, 0);
+            const int mode = rng() % 3;
+            if (mode == 0) {
+                std::vector<int64_t> cut(batch - 1);
+                for (auto &x : cut) x = (int64_t)(rng() % (uint64_t)(L + 1));
+                std::sort(cut.begin(), cut.end());
+                int64_t prev = 0;
+                for (int s = 0; s < batch - 1; ++s) { len[s] = cut[s] - prev; prev = cut[s]; }
+                len[batch - 1] = L - prev;
+            } else {
+                const int64_t each = mode == 1 ? p.chunk + 1 : 1;
+                int64_t left = L;
+                for (int s = 0; s < batch - 1 && left >= each; ++s) { len[s] = each; left -= each; }
+                len[batch - 1] += left;
+            }
+            int64_t sc = 0, su = 0, sg = 0, maxc = 0, maxs = 0;
+            const int64_t R = p.chunk / p.sub;
+            for (int64_t x : len) {   // the device's counts per sequence
+                const int64_t nc = (x + p.chunk - 1) / p.chunk;
+                const int64_t ns = nc >= 2 ? (nc - 1) * R + 1 : 0;
+                sc += nc; su += ns; sg += (ns + p.scan_group - 1) / p.scan_group;
+                maxc = std::max(maxc, nc);
+                maxs = std::max(maxs, ns);
+            }
+            ok = ok && sc <= p.nchunk_ub && su <= p.nsub_ub && sg <= p.ntile_ub &&
+                 (!p.single_chunk || maxc <= 1) &&
+                 (p.scan_tiles || maxs <= p.scan_group);   // untiled: one tile per sequence
         }
         if (!ok && bad++ < 10)
             printf("bad: b=%d h=%d L=%lld d=%d B=%d varlen=%d -> C=%lld S=%lld single=%d\n", batch, heads,

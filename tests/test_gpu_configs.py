@@ -84,9 +84,10 @@ def test_long_1m_two_heads(dev):
         assert err <= TOL["bf16"], h
 
 
-def test_varlen16(dev):
+@pytest.mark.parametrize("name", ["varlen16", "varlen_short"])
+def test_varlen_workload(dev, name):
     import torch
-    w = synth.WORKLOADS["varlen16"]
+    w = synth.WORKLOADS[name]
     note(f"workload {w.name}")
     lengths = synth.varlen_lengths(w.batch, w.len_seed, w.len_lo, w.len_hi)
     q, k, v, cu = synth.varlen_inputs(lengths, w.heads, w.head_dim, w.dtype, w.cid, dev)
@@ -97,7 +98,7 @@ def test_varlen16(dev):
     ref = oracle.causal_linear_attention_varlen(sel(q), sel(k), sel(v), cu, "recurrent",
                                                 nthreads=NTHREADS)
     err = oracle.rel_err(sel(o), ref)
-    print(f"varlen16 T={int(cu[-1])} rel_err={err:.3e}")
+    print(f"{name} T={int(cu[-1])} rel_err={err:.3e}")
     assert err <= TOL["bf16"]
 
 

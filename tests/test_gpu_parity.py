@@ -48,11 +48,13 @@ def test_random_small(dev, dt, d, B, n):
 @pytest.mark.parametrize("B,C,S,n", [(64, 64, 0, 64 * 40 + 7), (256, 256, 0, 256 * 34 + 100),
                                      (128, 512, 0, 5000), (256, 1024, 0, 3000),
                                      (64, 256, 64, 64 * 40 + 7), (256, 1024, 256, 256 * 34 + 100),
-                                     (128, 2048, 512, 5000)])
+                                     (128, 2048, 512, 5000), (64, 192, 64, 64 * 40 + 7),
+                                     (128, 640, 128, 9000)])
 def test_multi_chunk_and_scan_tiles(dev, dt, d, B, C, S, n):
     """Forced chunk lengths: many chunks per sequence (> 32 runs the tiled scan);
     S > 0 also forces the summary sub-chunk, so a chunk starts from the prefix
-    of several sub-chunk summaries."""
+    of several sub-chunk summaries.  With 3 and 5 sub-chunks per chunk the
+    scan tiles of 32 entries begin inside chunks."""
     note(f"multi_chunk dt={dt} d={d} B={B} C={C} S={S} n={n}")
     q, k, v = randn_qkv((1, 2, n, d), dt, 7 * n + d, dev)
     with chunk_tokens(C, S):
