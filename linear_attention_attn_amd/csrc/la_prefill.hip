@@ -571,9 +571,15 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(KParams p) {
     p.tilesum[((int64_t)h * p.ntile_ub + tile) * (D * D) + e] = acc;
 }
 
+// (B runs on the tile grid: the workgroup of a sequence's first tile scans
+// that sequence's tile totals, the others have nothing to do.)
 template <int D>
 __global__ __launch_bounds__(kScanThreads) void k_scan_tiles(KParams p) {
-    const int h = blockIdx.z, s = blockIdx.x;
+    const int h = blockIdx.z;
+    const int64_t tile = blockIdx.x;
+    if (tile >= p.tile_off[p.nseq]) return;
+    const int s = find_seg(p.tile_off, p.nseq, tile);
+    if (tile != p.tile_off[s]) return;
     const int e = blockIdx.y * kScanThreads + threadIdx.x;
     float *ts = p.tilesum + (int64_t)h * p.ntile_ub * (D * D) + e;
     float run = 0.f;
@@ -1642,8 +1648,7 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
         const dim3 gtiles((unsigned)plan.ntile_ub, (D * D) / kScanThreads, (unsigned)kp.heads);
         if (plan.scan_tiles) {
             hipLaunchKernelGGL(k_scan_reduce<D>, gtiles, dim3(kScanThreads), 0, st, kp);
-            hipLaunchKernelGGL(k_scan_tiles<D>, dim3(kp.nseq, (D * D) / kScanThreads, kp.heads),
-                               dim3(kScanThreads), 0, st, kp);
+            hipLaunchKernelGGL(k_scan_tiles<D>, gtiles, dim3(kScanThreads), 0, st, kp);
         }
         hipLaunchKernelGGL(k_scan_apply<D>, gtiles, dim3(kScanThreads), 0, st, kp, plan.scan_tiles ? 1 : 0);
     }

@@ -103,6 +103,28 @@ def test_state_packed_with_empty_sequences(dev, dt):
             assert np.array_equal(host(Sf)[s], host(S0)[s])
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_state_packed_tiled_scan(dev, dt, d):
+    """Packed sequences with several scan tiles each (79, 33 and 11 sub-chunk
+    entries with tiles of 32) next to one-chunk and empty ones, from initial
+    states, with two sub-chunks per chunk."""
+    import torch
+    lengths = (5000, 3, 2100, 0, 700, 64)
+    note(f"state packed tiled scan dt={dt} d={d}")
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T, H = int(cu[-1]), 2
+    q, k, v = randn_qkv((H, T, d), dt, 4545 + d, dev)
+    S0 = _states((len(lengths), H, d, d), 4646 + d, dev)
+    Sf = torch.full_like(S0, float("nan"))
+    cu_d = torch.tensor(cu, dtype=torch.int32, device=dev)
+    with chunk_tokens(128, 64):
+        o = host(_run(q, k, v, 64, S0, Sf, cu_d))
+    ref, sref = oracle.causal_linear_attention_varlen_state(host(q), host(k), host(v), cu, host(S0))
+    assert oracle.rel_err(o, ref) <= TOL[dt]
+    assert oracle.rel_err(host(Sf), sref) <= STOL
+
+
 def test_no_tokens_copies_initial_state(dev):
     """seq_len == 0: only s_final is written, equal to s_init (no workspace)."""
     import torch
