@@ -1269,7 +1269,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     // ---- Q rows of the wave's slabs: lane (c, g) loads row 16 slab + c,
     // elements 8g..8g+7 of each 32-element group kc
     uint32_t qvo[C::NSW], ovo[C::NSW];
-    const bool odd = g & 1;
     // O store m writes columns 16 (ct0 + 2m) + 4g .. +7 (even g) or
     // 16 (ct0 + 2m + 1) + 4 (g - 1) .. +7 (odd g): 64 m bytes further on
     auto o_off = [&](int si, int cc, int gg) {
@@ -1413,10 +1412,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
                 const uint32_t e1 = pack_bf16x2(O[si][2 * m][2], O[si][2 * m][3]);
                 const uint32_t o0 = pack_bf16x2(O[si][2 * m + 1][0], O[si][2 * m + 1][1]);
                 const uint32_t o1 = pack_bf16x2(O[si][2 * m + 1][2], O[si][2 * m + 1][3]);
-                const uint32_t r0 = (uint32_t)__shfl_xor((int)(odd ? e0 : o0), 16);
-                const uint32_t r1 = (uint32_t)__shfl_xor((int)(odd ? e1 : o1), 16);
-                const u32x4_t val = odd ? u32x4_t{r0, r1, o0, o1} : u32x4_t{e0, e1, r0, r1};
-                store16(ro, (uint32_t)(vo + m * 64), val);
+                // v_permlane16_swap exchanges the odd 16-lane rows of its first
+                // operand with the even rows of its second: an even-g lane keeps
+                // its even-tile words and gets its odd-g partner's, an odd-g lane
+                // gets its partner's odd-tile words and keeps its own
+                const auto x0 = __builtin_amdgcn_permlane16_swap(e0, o0, false, false);
+                const auto x1 = __builtin_amdgcn_permlane16_swap(e1, o1, false, false);
+                store16(ro, (uint32_t)(vo + m * 64), u32x4_t{x0[0], x1[0], x0[1], x1[1]});
             }
         }
     };
