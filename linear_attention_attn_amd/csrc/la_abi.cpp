@@ -150,6 +150,8 @@ void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int bloc
         off = align256(off + (size_t)batch * sizeof(int32_t));
         p.off_rank_off = off;
         off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));
+        p.off_slot_tab = off;
+        off = align256(off + (size_t)p.nchunk_ub * 2 * sizeof(int32_t));
     }
     p.off_tile_off = off;
     off = align256(off + (size_t)(batch + 1) * sizeof(int32_t));

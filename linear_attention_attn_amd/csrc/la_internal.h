@@ -27,6 +27,7 @@ struct FwdPlan {
     size_t off_err = 0;       // int32: 1 when cu_seqlens was found malformed (packed input)
     size_t off_perm = 0;      // int32 [nseq] (packed input: sequences longest first)
     size_t off_rank_off = 0;  // int32 [nseq + 1]
+    size_t off_slot_tab = 0;  // int32 [nchunk_ub][2] (packed input: sequence and chunk of each chunk slot)
     size_t off_tile_off = 0;  // int32 [nseq + 1]
     size_t off_states = 0;    // fp32 [heads][nsub_ub][d][d]
     size_t off_tilesum = 0;   // fp32 [heads][ntile_ub][d][d]

@@ -43,6 +43,9 @@ struct KParams {
     // sequences ranked before r
     int32_t *perm;          // [nseq]
     int32_t *rank_off;      // [nseq + 1]
+    // the same order as a direct table (packed input; nullptr for dense):
+    // slot_tab[2 r], slot_tab[2 r + 1] = sequence and global chunk of slot r
+    int32_t *slot_tab;      // [nchunk_ub][2]
     int32_t *sub_off;       // [nseq + 1] sub-chunks before each sequence
     int32_t *tile_off;      // [nseq + 1] scan tiles before each sequence
     int32_t *err;           // set to 1 by k_prep when cu_seqlens is malformed
@@ -115,13 +118,13 @@ __device__ __forceinline__ bool chunk_of_block(const KParams &p, int &h, int64_t
     h = (int)(lin % p.heads);
     const int64_t slot = lin / p.heads;
     if (slot >= p.chunk_off[p.nseq]) return false;
-    if (p.perm != nullptr) {
-        const int r = find_seg(p.rank_off, p.nseq, slot);
-        s = p.perm[r];
-        gch = p.chunk_off[s] + (slot - p.rank_off[r]);
-    } else {
+    if (p.slot_tab != nullptr) {        // one load instead of a search over the ranking
+        const int2 e = reinterpret_cast<const int2 *>(p.slot_tab)[slot];
+        s = e.x;
+        gch = e.y;
+    } else {                            // dense: every sequence has the same chunk count
         gch = slot;
-        s = find_seg(p.chunk_off, p.nseq, gch);
+        s = (int)(gch / ((p.seq_len + p.chunk - 1) / p.chunk));
     }
     return true;
 }
@@ -306,6 +309,12 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(KParams p) {
         p.rank_off[r] = (int32_t)cr;
         int64_t nc, ns, ng;
         counts(sq, nc, ns, ng);
+        // chunk_off was written by other threads before the barriers above
+        const int32_t c0 = p.chunk_off[sq];
+        for (int64_t i = 0; i < nc; ++i) {
+            p.slot_tab[2 * (cr + i)] = sq;
+            p.slot_tab[2 * (cr + i) + 1] = c0 + (int32_t)i;
+        }
         cr += nc;
     }
     if (t == kPrepThreads - 1) p.rank_off[n] = (int32_t)sc[t];
@@ -1708,6 +1717,7 @@ int launch_fwd(const FwdArgs &a, void *stream, void *const *events) {
     kp.sub_off = reinterpret_cast<int32_t *>(a.workspace + a.plan.off_sub_off);
     kp.perm = a.cu_seqlens ? reinterpret_cast<int32_t *>(a.workspace + a.plan.off_perm) : nullptr;
     kp.rank_off = a.cu_seqlens ? reinterpret_cast<int32_t *>(a.workspace + a.plan.off_rank_off) : nullptr;
+    kp.slot_tab = a.cu_seqlens ? reinterpret_cast<int32_t *>(a.workspace + a.plan.off_slot_tab) : nullptr;
     kp.tile_off = reinterpret_cast<int32_t *>(a.workspace + a.plan.off_tile_off);
     kp.err = a.cu_seqlens ? reinterpret_cast<int32_t *>(a.workspace + a.plan.off_err) : nullptr;
     kp.states = reinterpret_cast<float *>(a.workspace + a.plan.off_states);
