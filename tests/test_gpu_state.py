@@ -125,6 +125,27 @@ def test_state_packed_tiled_scan(dev, dt, d):
     assert oracle.rel_err(host(Sf), sref) <= STOL
 
 
+@pytest.mark.parametrize("C,S", [(128, 0), (256, 64), (192, 64)])
+def test_state_packed_chunk_boundaries(dev, C, S):
+    """Sequence lengths on both sides of one and two chunks (C, C + 1, 2C - 1,
+    2C, 2C + 1, 1 and 0 tokens) from initial states: the sequences of one
+    chunk read their initial state directly, the others through the scan."""
+    import torch
+    lengths = (C, C + 1, 2 * C - 1, 2 * C, 2 * C + 1, 1, 0, 3 * C + 5)
+    note(f"state packed chunk boundaries C={C} S={S}")
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T, H, d = int(cu[-1]), 2, 64
+    q, k, v = randn_qkv((H, T, d), "bf16", 4747 + C, dev)
+    S0 = _states((len(lengths), H, d, d), 4848 + C, dev)
+    Sf = torch.full_like(S0, float("nan"))
+    cu_d = torch.tensor(cu, dtype=torch.int32, device=dev)
+    with chunk_tokens(C, S):
+        o = host(_run(q, k, v, 64, S0, Sf, cu_d))
+    ref, sref = oracle.causal_linear_attention_varlen_state(host(q), host(k), host(v), cu, host(S0))
+    assert oracle.rel_err(o, ref) <= TOL["bf16"]
+    assert oracle.rel_err(host(Sf), sref) <= STOL
+
+
 def test_no_tokens_copies_initial_state(dev):
     """seq_len == 0: only s_final is written, equal to s_init (no workspace)."""
     import torch
