@@ -1,4 +1,4 @@
-"""Randomised parity: 120 seeded draws over the prefill's options at once
+"""Randomised parity: 240 seeded draws over the prefill's options at once
 (dtype, head dim, block size, dense or packed input with empty sequences,
 forced chunk and sub-chunk lengths, initial/final states or a pool with a
 slot table, the rotary prologue with position offsets), each against the CPU
@@ -52,7 +52,7 @@ def _draw(seed):
     return c
 
 
-@pytest.mark.parametrize("seed", range(120))
+@pytest.mark.parametrize("seed", range(240))
 def test_random_prefill(dev, seed):
     import torch
     import linear_attention_attn_amd as la
