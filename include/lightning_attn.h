@@ -89,8 +89,9 @@ int64_t lightning_attn_fwd_chunk_tokens(int batch, int heads, int64_t seq_len, i
  *
  * q, k, v, o and the workspace must be 16-byte aligned and cu_seqlens 4-byte
  * aligned (else LA_EINVAL; the kernels move 16-byte vectors).
- * All argument checks happen on the host before any launch; a rejected call
- * writes nothing.  seq_len == 0 returns LA_OK without touching any pointer.
+ * All argument checks happen on the host before any launch (the contents of
+ * cu_seqlens, which live on the device, are checked by the first kernel as
+ * described above); a rejected call writes nothing.  seq_len == 0 returns LA_OK without touching any pointer.
  * Device-side faults surface at the caller's next synchronisation.
  */
 int lightning_attn_fwd(const void *q, const void *k, const void *v, void *o,
