@@ -19,9 +19,10 @@
  * Plain C: no C++ or HIP types in any signature.  All tensor pointers are
  * DEVICE pointers on the current HIP device; `stream` is a hipStream_t passed
  * as void* (NULL = the default stream).  Every launch is asynchronous on
- * `stream`; nothing synchronises the host.  The library allocates no memory
- * and keeps no mutable global state, so calls are reentrant; calls that share
- * a workspace or a decode state must be ordered by the caller.
+ * `stream`; nothing synchronises the host.  The library allocates no memory;
+ * the only state it keeps is each device's compute-unit count, read once from
+ * the device's properties.  Calls are reentrant; calls that share a workspace
+ * or a decode state must be ordered by the caller.
  */
 #ifndef LIGHTNING_ATTN_H
 #define LIGHTNING_ATTN_H
@@ -49,7 +50,9 @@ extern "C" {
  * (always a multiple of 256; 0 when seq_len == 0).  `varlen` is non-zero when
  * cu_seqlens will be passed; then `batch` is the number of packed sequences
  * and `seq_len` their total token count.  Returns 0 for arguments
- * lightning_attn_fwd would reject.  The workspace holds per-chunk fp32 d x d
+ * lightning_attn_fwd would reject.  The work is split to fill the current
+ * device's compute units, so query with the device current that will run the
+ * pass.  The workspace holds per-chunk fp32 d x d
  * states (Tencent Cloud article, section 4.1: the compact key-value prefix of
  * all earlier blocks) and small tables; its contents need no initialisation
  * and are scratch after the call.
@@ -249,6 +252,43 @@ int lightning_attn_decode_rope(const void *q, const void *k, const void *v, floa
                                int nslots, const int32_t *slots, void *o, int batch, int heads,
                                int head_dim, int dtype, int rope_dims, double rope_base,
                                const int32_t *positions, void *stream);
+
+/*
+ * Test hooks: the forward pass with the chunking fixed by the caller instead
+ * of chosen by the library, so that tests can reach every path of the
+ * parallel scan (many chunks per sequence, many summary sub-chunks per chunk,
+ * scan tiles starting inside chunks) at small sizes.  The result does not
+ * depend on the chunking beyond rounding.  Not for production use: the
+ * library's own choice (lightning_attn_fwd and the others) is the fast one.
+ *   chunk_tokens: 0 (the library's choice) or the tokens one workgroup walks
+ *                 carrying the state: a positive multiple of block_size, at
+ *                 most 2^30 / (2 head_dim) tokens, and a multiple of 16384
+ *                 when above 16384;
+ *   sub_tokens:   0 (the library's choice) or the tokens of one K^T V summary:
+ *                 a multiple of block_size dividing the chunk (ignored when
+ *                 one chunk covers every dense sequence).
+ * Other values are LA_EINVAL, and the size query returns 0 for them.
+ *
+ * lightning_attn_fwd_planned takes the union of the other forward entry
+ * points' options: with slots == NULL, s_init / s_final as
+ * lightning_attn_fwd_state (state_pool must be NULL); with slots != NULL, the
+ * indexed pool of lightning_attn_fwd_indexed (s_init and s_final must be
+ * NULL); rope_dims 0 or head_dim / 2 with rope_base and pos_offset as
+ * lightning_attn_fwd_rope.  The workspace must be at least
+ * lightning_attn_fwd_workspace_size_planned(...) bytes for the same
+ * chunk_tokens and sub_tokens.  Everything else is as lightning_attn_fwd.
+ */
+size_t lightning_attn_fwd_workspace_size_planned(int batch, int heads, int64_t seq_len, int head_dim,
+                                                 int block_size, int varlen, int dtype,
+                                                 int64_t chunk_tokens, int64_t sub_tokens);
+int lightning_attn_fwd_planned(const void *q, const void *k, const void *v, void *o,
+                               int batch, int heads, int64_t seq_len, int head_dim, int block_size,
+                               const int32_t *cu_seqlens, int dtype,
+                               const float *s_init, float *s_final,
+                               float *state_pool, int nslots, const int32_t *slots,
+                               int rope_dims, double rope_base, const int32_t *pos_offset,
+                               int64_t chunk_tokens, int64_t sub_tokens,
+                               void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static, human-readable text for a status code. */
 const char *lightning_attn_strerror(int status);

@@ -48,39 +48,46 @@ static int64_t env_i64(const char *name, int64_t dflt) {
 //
 // Dense input: every candidate C is priced with a simple model of the two
 // passes in units of "tokens one CU streams through the fused kernel":
-//   fused   = ceil(units * n / kCUs) * C      (rounds of one chunk per CU)
-//   summary = kSum * units * (n - 1) * C / kCUs   (every chunk but the last is
+//   fused   = ceil(units * n / cus) * C      (rounds of one chunk per CU)
+//   summary = kSum * units * (n - 1) * C / cus   (every chunk but the last is
 //             summarised; measured ~0.45 of the fused cost per token)
-//   scan    = kScan * units * n_s / kCUs      (three passes over 64 KiB fp32
+//   scan    = kScan * units * n_s / cus      (three passes over 64 KiB fp32
 //             states per sub-chunk, ~190 token-equivalents each)
 // with n = ceil(L / C) chunks and n_s = ceil(L / C_s) sub-chunks per unit.
 // Candidates: one chunk per sequence (no summary or scan at all), powers of
 // two from the block size to kSub, and multiples of kSub (sub-chunks of kSub),
 // all within the 32-bit buffer offsets of the bf16 kernels (2^30 bytes of a
-// chunk's rows).  E.g. 64 heads x 1M tokens: C = 262144 (4 chunks per head,
-// one workgroup per CU) with sub-chunks of 16384, so the summaries read 3/4
-// of k and v instead of 63/64 with 16384-token chunks.
+// chunk's rows).  E.g. 64 heads x 1M tokens on 256 CUs: C = 262144 (4 chunks
+// per head, one workgroup per CU) with sub-chunks of 16384, so the summaries
+// read 3/4 of k and v instead of 63/64 with 16384-token chunks.
 //
 // Packed input (the lengths live on the device): C = the largest power of
-// two <= W / kCUs (W = all head-tokens), so that there are at least about
-// kCUs chunks and no chunk is longer than a CU's average share; sub-chunks of
+// two <= W / cus (W = all head-tokens), so that there are at least about
+// cus chunks and no chunk is longer than a CU's average share; sub-chunks of
 // at most kSub.  The fused kernel takes the chunks of the longest sequences
 // first, so the long ones do not start last.
 //
-// LA_CHUNK_TOKENS forces C (a multiple of the block size, and of kSub above
-// it); LA_SUB_TOKENS forces C_s (a multiple of the block size dividing C).
-void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int block_size, bool varlen,
-                   FwdPlan *plan) {
-    const int64_t kCUs = env_i64("LA_TARGET_GROUPS", 256);
+// An override (test entry point only) fixes C: a multiple of the block size
+// within the offset cap, and above kSub a multiple of kSub; and C_s: a
+// multiple of the block size dividing C (ignored when one chunk covers every
+// dense sequence).  Anything else is LA_EINVAL.
+int make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int block_size, bool varlen,
+                  int cus, const PlanOverride &ov, FwdPlan *plan) {
+    const int64_t kCUs = cus > 0 ? cus : 256;
     const int64_t kSub = 16384;
     const double kSum = 0.45, kScan = 190.0;
     const int64_t units = (int64_t)batch * heads;
     const int64_t B = block_size;
     const int64_t cap = (((int64_t)1 << 30) / (head_dim * 2)) / B * B;
     auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
+    if (ov.chunk < 0 || ov.sub < 0) return LA_EINVAL;
 
     int64_t C;
-    if (!varlen) {
+    if (ov.chunk > 0) {
+        if (ov.chunk % B != 0 || ov.chunk > cap || (ov.chunk > kSub && ov.chunk % kSub != 0))
+            return LA_EINVAL;
+        C = ov.chunk;
+    } else if (!varlen) {
         const int64_t L = std::max<int64_t>(1, seq_len);
         auto cost = [&](int64_t c) {
             const int64_t n = cdiv(L, c);
@@ -106,15 +113,12 @@ void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int bloc
         C = B;
         while (C * 2 <= cap && C * 2 <= per_cu) C *= 2;
     }
-    const int64_t forced = env_i64("LA_CHUNK_TOKENS", 0);
-    if (forced > 0) {
-        C = std::max<int64_t>(B, std::min(cap, forced / B * B));
-        if (C > kSub) C = C / kSub * kSub;
-    }
     const bool one = !varlen && cdiv(std::max<int64_t>(1, seq_len), C) == 1;
     int64_t Cs = one ? C : std::min(C, kSub);
-    const int64_t fs = env_i64("LA_SUB_TOKENS", 0);
-    if (fs > 0 && !one && fs % B == 0 && fs <= C && C % fs == 0) Cs = fs;
+    if (ov.sub > 0 && !one) {
+        if (ov.sub % B != 0 || C % ov.sub != 0) return LA_EINVAL;
+        Cs = ov.sub;
+    }
 
     const int G = 32;
     FwdPlan p;
@@ -161,6 +165,7 @@ void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int bloc
     if (p.scan_tiles) off = align256(off + (size_t)heads * (size_t)p.ntile_ub * dd);
     p.bytes = off;
     *plan = p;
+    return LA_OK;
 }
 
 }  // namespace la
@@ -169,10 +174,22 @@ extern "C" {
 
 size_t lightning_attn_fwd_workspace_size(int batch, int heads, int64_t seq_len, int head_dim,
                                          int block_size, int varlen, int dtype) {
+    return lightning_attn_fwd_workspace_size_planned(batch, heads, seq_len, head_dim, block_size, varlen,
+                                                     dtype, 0, 0);
+}
+
+size_t lightning_attn_fwd_workspace_size_planned(int batch, int heads, int64_t seq_len, int head_dim,
+                                                 int block_size, int varlen, int dtype,
+                                                 int64_t chunk_tokens, int64_t sub_tokens) {
     if (la::check_fwd_shape(batch, heads, seq_len, head_dim, block_size, dtype) != LA_OK) return 0;
     if (seq_len == 0) return 0;
     la::FwdPlan p;
-    la::make_fwd_plan(batch, heads, seq_len, head_dim, block_size, varlen != 0, &p);
+    la::PlanOverride ov;
+    ov.chunk = chunk_tokens;
+    ov.sub = sub_tokens;
+    if (la::make_fwd_plan(batch, heads, seq_len, head_dim, block_size, varlen != 0, la::device_cu_count(),
+                          ov, &p) != LA_OK)
+        return 0;
     return p.bytes;
 }
 
@@ -181,7 +198,8 @@ int64_t lightning_attn_fwd_chunk_tokens(int batch, int heads, int64_t seq_len, i
     if (la::check_fwd_shape(batch, heads, seq_len, head_dim, block_size, dtype) != LA_OK) return 0;
     if (seq_len == 0) return 0;
     la::FwdPlan p;
-    la::make_fwd_plan(batch, heads, seq_len, head_dim, block_size, varlen != 0, &p);
+    la::make_fwd_plan(batch, heads, seq_len, head_dim, block_size, varlen != 0, la::device_cu_count(),
+                      la::PlanOverride{}, &p);
     return p.chunk;
 }
 
@@ -198,7 +216,8 @@ static int fwd_common(const void *q, const void *k, const void *v, void *o, int 
                       int dtype, const float *s_init, float *s_final, void *workspace,
                       size_t workspace_bytes, void *stream, void *const *events,
                       int rope_dims = 0, double rope_base = 0.0, const int32_t *pos0 = nullptr,
-                      const int32_t *slots = nullptr, int nslots = 0) {
+                      const int32_t *slots = nullptr, int nslots = 0,
+                      la::PlanOverride ov = la::PlanOverride{}) {
     int st = la::check_fwd_shape(batch, heads, seq_len, head_dim, block_size, dtype);
     if (st != LA_OK) return st;
     st = check_rope(rope_dims, rope_base, head_dim);
@@ -220,7 +239,9 @@ static int fwd_common(const void *q, const void *k, const void *v, void *o, int 
     a.s_init = s_init; a.s_final = s_final;
     a.rope_dims = rope_dims; a.rope_base = rope_base; a.pos0 = pos0;
     a.slots = slots; a.nslots = nslots;
-    la::make_fwd_plan(batch, heads, seq_len, head_dim, block_size, cu_seqlens != nullptr, &a.plan);
+    st = la::make_fwd_plan(batch, heads, seq_len, head_dim, block_size, cu_seqlens != nullptr,
+                           la::device_cu_count(), ov, &a.plan);
+    if (st != LA_OK) return st;
     if (!workspace || workspace_bytes < a.plan.bytes) return LA_EWORKSPACE;
     if (((uintptr_t)workspace & 255) != 0) return LA_EINVAL;
     a.workspace = static_cast<char *>(workspace);
@@ -271,6 +292,30 @@ int lightning_attn_fwd_indexed(const void *q, const void *k, const void *v, void
     return fwd_common(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens, dtype,
                       state_pool, state_pool, workspace, workspace_bytes, stream, nullptr, rope_dims,
                       rope_base, pos_offset, slots, nslots);
+}
+
+int lightning_attn_fwd_planned(const void *q, const void *k, const void *v, void *o, int batch,
+                               int heads, int64_t seq_len, int head_dim, int block_size,
+                               const int32_t *cu_seqlens, int dtype, const float *s_init,
+                               float *s_final, float *state_pool, int nslots, const int32_t *slots,
+                               int rope_dims, double rope_base, const int32_t *pos_offset,
+                               int64_t chunk_tokens, int64_t sub_tokens, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    la::PlanOverride ov;
+    ov.chunk = chunk_tokens;
+    ov.sub = sub_tokens;
+    if (rope_dims < 0) return LA_EUNSUPPORTED;
+    if (slots) {
+        if (s_init || s_final || nslots < 0 || (nslots > 0 && !state_pool)) return LA_EINVAL;
+        if ((int64_t)nslots * heads > (int64_t)INT32_MAX) return LA_EUNSUPPORTED;
+        return fwd_common(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens, dtype,
+                          state_pool, state_pool, workspace, workspace_bytes, stream, nullptr, rope_dims,
+                          rope_base, pos_offset, slots, nslots, ov);
+    }
+    if (state_pool) return LA_EINVAL;
+    return fwd_common(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens, dtype, s_init,
+                      s_final, workspace, workspace_bytes, stream, nullptr, rope_dims, rope_base,
+                      pos_offset, nullptr, 0, ov);
 }
 
 int lightning_attn_fwd_traced(const void *q, const void *k, const void *v, void *o, int batch,

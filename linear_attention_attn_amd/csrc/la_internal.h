@@ -39,9 +39,25 @@ struct FwdPlan {
 int check_fwd_shape(int batch, int heads, int64_t seq_len, int head_dim, int block_size,
                     int dtype);
 
-// Fill *plan for a checked shape (seq_len > 0).
-void make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int block_size,
-                   bool varlen, FwdPlan *plan);
+// Chunk and sub-chunk lengths given by the caller instead of chosen by the
+// planner (0 = the planner's choice).  Only the test entry point
+// lightning_attn_fwd_planned sets them; nothing reads them from the
+// environment.
+struct PlanOverride {
+    int64_t chunk = 0;
+    int64_t sub = 0;
+};
+
+// Fill *plan for a checked shape (seq_len > 0) on a device with `cus`
+// compute units.  Returns LA_OK, or LA_EINVAL when an override is not a
+// valid chunk / sub-chunk length for the shape (then *plan is untouched).
+int make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int block_size,
+                  bool varlen, int cus, const PlanOverride &ov, FwdPlan *plan);
+
+// Compute units of the current HIP device, read once per device from its
+// properties and cached (256 when no device can be queried, e.g. a host
+// without a GPU).
+int device_cu_count();
 
 struct FwdArgs {
     const void *q, *k, *v;

@@ -28,6 +28,8 @@
 // intra-block partial never goes to memory.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "la_common.h"
 #include "la_internal.h"
 
@@ -1683,6 +1685,27 @@ static hipError_t launch_blk(const KParams &kp, const FwdPlan &plan, int blk, hi
         case 128: return launch_typed<T, D, 128, ROPE>(kp, plan, st, ev);
         default: return launch_typed<T, D, 256, ROPE>(kp, plan, st, ev);
     }
+}
+
+// Compute units of the current device, queried once per device and cached
+// (the only state the library keeps).  A partitioned GPU reports its own
+// share, so the plan balances chunks over the CUs that actually run them.
+int device_cu_count() {
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cached[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 int read_cu_error(const FwdArgs &a, void *stream, int *flag) {

@@ -1,6 +1,5 @@
 """Helpers for the GPU parity tests (HIP path vs the CPU oracle)."""
 import math
-import os
 import sys
 
 import numpy as np
@@ -47,23 +46,22 @@ def host(x):
 
 
 class chunk_tokens:
-    """Temporarily force the library's chunk length (LA_CHUNK_TOKENS) and,
-    optionally, its sub-chunk (summary) length (LA_SUB_TOKENS)."""
+    """Inside the block, ``linear_attention_attn_amd.fwd`` runs with the
+    chunking fixed (chunk length n tokens and, optionally, the summary
+    sub-chunk length) through the library's test entry point
+    lightning_attn_fwd_planned; 0 leaves the library's choice."""
 
     def __init__(self, n, sub=0):
-        self.vals = {"LA_CHUNK_TOKENS": n, "LA_SUB_TOKENS": sub}
+        self.n, self.sub = n, sub
 
     def __enter__(self):
-        self.old = {k: os.environ.get(k) for k in self.vals}
-        for k, v in self.vals.items():
-            if v:
-                os.environ[k] = str(v)
-            else:
-                os.environ.pop(k, None)
+        import functools
+        import linear_attention_attn_amd as la
+        self.orig = la.fwd
+        if self.n or self.sub:
+            la.fwd = functools.partial(self.orig, chunk_tokens=self.n, sub_tokens=self.sub)
+        return self
 
     def __exit__(self, *a):
-        for k, v in self.old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+        import linear_attention_attn_amd as la
+        la.fwd = self.orig

@@ -5,7 +5,8 @@
 // slot counts match the dense shape; for packed input, over random and
 // adversarial splits of the tokens into sequences, the chunk, sub-chunk and
 // scan-tile counts the device derives from the lengths stay within the plan's
-// bounds.  Built with g++ against stubs of the launchers; run by
+// bounds; explicit chunk / sub-chunk overrides are honoured when valid and
+// rejected otherwise.  Built with g++ against stubs of the launchers; run by
 // tests/test_plan_host.py.
 #include <cstdio>
 #include <cstdlib>
@@ -19,6 +20,7 @@ int launch_state_empty(const float *, float *, int, int, int, void *) { return 0
 int read_cu_error(const FwdArgs &, void *, int *flag) { *flag = 0; return 0; }
 int launch_decode(const void *, const void *, const void *, float *, void *, int, int, int, int, void *,
                   const int32_t *, int, int, double, const int32_t *) { return 0; }
+int device_cu_count() { return 256; }
 }
 int main() {  // exit status 0 when every plan passes
     std::mt19937_64 rng(1);
@@ -30,8 +32,13 @@ int main() {  // exit status 0 when every plan passes
         int64_t L = 1 + (int64_t)(rng() % (1ull << (1 + rng() % 27)));
         if (varlen) L = L * (1 + rng() % 4);
         if (L > 2000000000LL) L = 2000000000LL;
+        // whole GPUs and partitions of one (fewer compute units)
+        const int cus = (rng() & 3) ? 256 : 32 + (int)(rng() % 225);
         la::FwdPlan p;
-        la::make_fwd_plan(batch, heads, L, d, B, varlen, &p);
+        if (la::make_fwd_plan(batch, heads, L, d, B, varlen, cus, la::PlanOverride{}, &p) != 0) {
+            if (bad++ < 10) printf("planner rejected b=%d h=%d L=%lld\n", batch, heads, (long long)L);
+            continue;
+        }
         ++n;
         const int64_t cap = ((1LL << 30) / (d * 2)) / B * B;
         bool ok = p.chunk >= B && p.chunk % B == 0 && p.chunk <= cap && p.sub >= B && p.sub % B == 0 &&
@@ -74,6 +81,37 @@ int main() {  // exit status 0 when every plan passes
         if (!ok && bad++ < 10)
             printf("bad: b=%d h=%d L=%lld d=%d B=%d varlen=%d -> C=%lld S=%lld single=%d\n", batch, heads,
                    (long long)L, d, B, (int)varlen, (long long)p.chunk, (long long)p.sub, (int)p.single_chunk);
+    }
+    // test-only overrides: a valid chunk / sub-chunk pair is taken as given,
+    // anything else is rejected with LA_EINVAL (1) and leaves the plan alone
+    for (int it = 0; it < 100000; ++it) {
+        int batch = 1 + rng() % 50, heads = 1 + rng() % 64;
+        int d = (rng() & 1) ? 64 : 128, B = 64 << (rng() % 3);
+        bool varlen = rng() & 1;
+        int64_t L = 1 + (int64_t)(rng() % (1ull << (1 + rng() % 22)));
+        const int64_t cap = ((1LL << 30) / (d * 2)) / B * B;
+        la::PlanOverride ov;
+        ov.chunk = (rng() & 7) ? (int64_t)B * (1 + rng() % 300) : (int64_t)(1 + rng() % 70000);
+        if (rng() & 1) ov.chunk = 16384 * (1 + rng() % 8);
+        ov.sub = (rng() & 1) ? 0 : ((rng() & 3) ? ov.chunk / (1 + rng() % 4) : (int64_t)(1 + rng() % 5000));
+        const bool cvalid = ov.chunk % B == 0 && ov.chunk <= cap && (ov.chunk <= 16384 || ov.chunk % 16384 == 0);
+        const bool one = !varlen && (L + ov.chunk - 1) / ov.chunk == 1;
+        const bool svalid = ov.sub == 0 || one || (ov.sub % B == 0 && ov.chunk % ov.sub == 0);
+        la::FwdPlan p;
+        p.chunk = -7;
+        const int st = la::make_fwd_plan(batch, heads, L, d, B, varlen, 256, ov, &p);
+        ++n;
+        bool ok;
+        if (cvalid && svalid) {
+            ok = st == 0 && p.chunk == ov.chunk &&
+                 p.sub == (one ? ov.chunk : (ov.sub ? ov.sub : std::min<int64_t>(ov.chunk, 16384)));
+        } else {
+            ok = st == 1 && p.chunk == -7;
+        }
+        if (!ok && bad++ < 10)
+            printf("override: b=%d L=%lld B=%d C=%lld S=%lld varlen=%d -> st=%d C=%lld S=%lld\n", batch,
+                   (long long)L, B, (long long)ov.chunk, (long long)ov.sub, (int)varlen, st,
+                   (long long)p.chunk, (long long)p.sub);
     }
     printf("%ld plans, %ld bad\n", n, bad);
     return bad != 0;

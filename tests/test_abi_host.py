@@ -169,6 +169,51 @@ def test_fwd_indexed_rejects(la):
                                          0, 1e4, None, None, 0, None) == 0   # no tokens: nothing to do
 
 
+def test_planned_overrides(la):
+    """The test entry point takes a chunking only when it is valid for the
+    shape; the size query returns 0 and the call LA_EINVAL otherwise, before
+    any launch."""
+    wsp = la.lightning_attn_fwd_workspace_size_planned
+    # the library's own choice when nothing is forced
+    assert wsp(4, 64, 8192, 128, 256, 0, 0, 0, 0) == la.lightning_attn_fwd_workspace_size(4, 64, 8192, 128,
+                                                                                          256, 0, 0)
+    assert wsp(1, 2, 5000, 64, 128, 0, 0, 512, 0) > 0
+    assert wsp(1, 2, 5000, 64, 128, 0, 0, 512, 128) > wsp(1, 2, 5000, 64, 128, 0, 0, 512, 0)
+    for C, S in ((500, 0), (64, 0), (512, 96), (512, 384), (16384 + 256, 0), (-256, 0), (512, -128)):
+        assert wsp(1, 2, 5000, 64, 128, 0, 0, C, S) == 0, (C, S)
+    assert wsp(1, 2, 100000, 64, 128, 1, 0, 32768, 16384) > 0       # multiples of 16384 above it
+    assert wsp(1, 2, 100, 64, 128, 0, 0, 512, 384) > 0              # one chunk: sub ignored
+
+    fake = 1 << 20
+    need = wsp(1, 2, 5000, 64, 128, 0, 0, 512, 128)
+
+    def fp(C=512, S=128, s_init=None, s_final=None, pool=None, nslots=0, slots=None, r=0, n=5000):
+        return la.lightning_attn_fwd_planned(fake, fake, fake, fake, 1, 2, n, 64, 128, None, 0, s_init,
+                                             s_final, pool, nslots, slots, r, 1e4, None, C, S, fake,
+                                             need, None)
+    assert fp(C=500) == 1
+    assert fp(S=96) == 1
+    assert fp(pool=fake) == 1                          # a pool without a slot table
+    assert fp(slots=fake, nslots=2, pool=fake, s_init=fake) == 1   # pool and s_init are exclusive
+    assert fp(slots=fake, nslots=2, pool=None) == 1
+    assert fp(r=16) == 2
+    assert fp(n=0) == 0                                # no tokens: nothing to do
+
+
+def test_no_plan_knobs_in_environment(monkeypatch, la):
+    """The plan does not depend on the caller's environment."""
+    base = [la.lightning_attn_fwd_workspace_size(1, 64, 1 << 20, 128, 256, 0, 0),
+            la.lightning_attn_fwd_chunk_tokens(1, 64, 1 << 20, 128, 256, 0, 0)]
+    for k, v in (("LA_CHUNK_TOKENS", "256"), ("LA_SUB_TOKENS", "256"), ("LA_TARGET_GROUPS", "7")):
+        monkeypatch.setenv(k, v)
+    assert [la.lightning_attn_fwd_workspace_size(1, 64, 1 << 20, 128, 256, 0, 0),
+            la.lightning_attn_fwd_chunk_tokens(1, 64, 1 << 20, 128, 256, 0, 0)] == base
+    for f in os.listdir(os.path.join(ROOT, "linear_attention_attn_amd", "csrc")):
+        txt = open(os.path.join(ROOT, "linear_attention_attn_amd", "csrc", f)).read()
+        for knob in ("LA_CHUNK_TOKENS", "LA_SUB_TOKENS", "LA_TARGET_GROUPS"):
+            assert knob not in txt, (f, knob)
+
+
 def test_product_never_imports_oracle():
     """The HIP path must not route through the CPU oracle."""
     pkg = os.path.join(ROOT, "linear_attention_attn_amd")

@@ -1,6 +1,22 @@
 """The five workloads at full size on the GPU, in the launch configuration the
-benchmark times, checked against the CPU oracle (in full where the oracle
-finishes in seconds, else on sampled heads, sequences or rows)."""
+benchmark times, checked against the CPU oracle on every output:
+
+* tiny fp32 (B1 H2 d64 n1024): against the naive and the recurrent form;
+* MiniMax layer (B4 H64 d128 n8192): all 256 (sequence, head) units;
+* long context (B1 H64 d128 n1,048,576): all 64 heads run; heads 0 and 63
+  checked on all 1,048,576 rows, the oracle walking each head once in slabs
+  of 65,536 rows with its fp64 state carried from slab to slab;
+* packed 16 sequences (T = 368,523) and the short packed mix: all 64 heads,
+  in groups of heads to bound host memory;
+* decode (256 sequences x 64 heads, 128 steps): all 16,384 states, every
+  step's output and the final states.
+
+Besides the stated metric max|o - o_ref| / max|o_ref| over the checked
+tensor, each check reports the same ratio per block (256 rows of a stream
+for the prefills, one state at one step for decode) and the worst block:
+|o| grows with the position (to about 90 at 1M tokens), so the whole-tensor
+ratio alone would barely constrain the early blocks.  The per-block ratio is
+held to the same bar."""
 import os
 import threading
 
@@ -14,6 +30,7 @@ from gpu_util import TOL, device, host, note
 pytestmark = pytest.mark.gpu
 
 NTHREADS = min(16, len(os.sched_getaffinity(0)))
+ROWS_PER_BLOCK = 256
 
 
 @pytest.fixture(scope="module")
@@ -29,6 +46,44 @@ def _fwd(q, k, v, B, cu=None):
     return o
 
 
+class ErrTracker:
+    """Running max|o - ref| and max|ref| over a tensor fed in row slabs, and
+    the same two maxima per block of `rows` rows (blocks start at row 0 of
+    each stream; `first_row` is the slab's first row in its stream)."""
+
+    def __init__(self, rows=ROWS_PER_BLOCK):
+        self.rows = rows
+        self.num = 0.0
+        self.den = 0.0
+        self.worst = (0.0, None)
+
+    def add(self, got, ref, first_row=0, label=""):
+        got = np.asarray(got, np.float64).reshape(-1, ref.shape[-1])
+        ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+        diff = np.abs(got - ref)
+        self.num = max(self.num, float(diff.max(initial=0.0)))
+        self.den = max(self.den, float(np.abs(ref).max(initial=0.0)))
+        n = ref.shape[0]
+        start = 0
+        while start < n:
+            blk = (first_row + start) // self.rows
+            end = min(n, (blk + 1) * self.rows - first_row)
+            den = float(np.abs(ref[start:end]).max(initial=0.0))
+            if den > 0:
+                e = float(diff[start:end].max()) / den
+                if e > self.worst[0]:
+                    self.worst = (e, f"{label} block {blk}")
+            start = end
+
+    @property
+    def err(self):
+        return self.num / self.den if self.den > 0 else self.num
+
+    def report(self, name):
+        print(f"{name}: rel_err={self.err:.3e}  worst per-block rel_err={self.worst[0]:.3e} "
+              f"({self.worst[1]})", flush=True)
+
+
 def test_tiny_f32(dev):
     w = synth.WORKLOADS["tiny_f32"]
     note(f"workload {w.name}")
@@ -38,7 +93,12 @@ def test_tiny_f32(dev):
     naive = oracle.causal_linear_attention(qh, kh, vh, "naive", nthreads=NTHREADS)
     rec = oracle.causal_linear_attention(qh, kh, vh, "recurrent", nthreads=NTHREADS)
     assert oracle.rel_err(naive, rec) < 1e-12
+    tr = ErrTracker(w.block_size)
+    for h in range(w.heads):
+        tr.add(o[0, h], naive[0, h], label=f"head {h}")
+    tr.report(w.name)
     assert oracle.rel_err(o, naive) <= TOL["f32"]
+    assert tr.worst[0] <= TOL["f32"]
 
 
 def test_minimax_layer_full(dev):
@@ -49,81 +109,126 @@ def test_minimax_layer_full(dev):
     qh, kh, vh = host(q), host(k), host(v)
     del q, k, v
     ref = oracle.causal_linear_attention(qh, kh, vh, "recurrent", nthreads=NTHREADS)
-    err = oracle.rel_err(host(o), ref)
-    print(f"minimax_layer rel_err={err:.3e}")
-    assert err <= TOL["bf16"]
+    oh = host(o)
+    tr = ErrTracker()
+    for b in range(w.batch):
+        for h in range(w.heads):
+            tr.add(oh[b, h], ref[b, h], label=f"seq {b} head {h}")
+    tr.report(w.name)
+    assert tr.err <= TOL["bf16"]
+    assert tr.worst[0] <= TOL["bf16"]
 
 
-def test_long_1m_two_heads(dev):
-    """Full 1,048,576-token run of all 64 heads; heads 0 and 63 checked at 512
-    sampled rows each (every block edge class, the first and last rows)."""
-    import torch
+def test_long_1m_two_heads_every_row(dev):
+    """All 64 heads of 1,048,576 tokens in one call; heads 0 and 63 compared
+    on every row (the oracle's recurrence walked once per head, in slabs)."""
     w = synth.WORKLOADS["long_1m"]
     note(f"workload {w.name}")
     q, k, v = synth.prefill_inputs(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype, w.cid, dev)
     o = _fwd(q, k, v, w.block_size)
-    n = w.seq_len
-    rng = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, 257, n // 2, n - 257, n - 256, n - 1],
-                                     rng.integers(0, n, 500)]))
-    results = {}
+    n, d, slab = w.seq_len, w.head_dim, 65536
+    heads = (0, 63)
+    inputs = {h: (host(q[0, h]), host(k[0, h]), host(v[0, h])) for h in heads}
+    del q, k, v
+    trackers = {h: ErrTracker() for h in heads}
+    errors = []
 
     def run(h):
-        results[h] = oracle.recurrent_rows(host(q[0, h]), host(k[0, h]), host(v[0, h]), rows)
+        try:
+            qh, kh, vh = inputs[h]
+            S = np.zeros((d, d))
+            for r0 in range(0, n, slab):
+                r1 = min(n, r0 + slab)
+                ref, S = oracle.recurrent_final_state(qh[r0:r1], kh[r0:r1], vh[r0:r1], S)
+                trackers[h].add(got_slabs[h][r0 // slab], ref, first_row=r0, label=f"head {h}")
+        except Exception as e:  # surfaced below
+            errors.append(e)
 
-    ths = [threading.Thread(target=run, args=(h,)) for h in (0, 63)]
+    # the GPU output of both heads, copied to the host slab by slab first
+    got_slabs = {h: [host(o[0, h, r0:min(n, r0 + slab)]) for r0 in range(0, n, slab)] for h in heads}
+    ths = [threading.Thread(target=run, args=(h,)) for h in heads]
     for t in ths:
         t.start()
     for t in ths:
         t.join()
-    rows_t = torch.from_numpy(rows).to(dev)
-    for h in (0, 63):
-        got = host(o[0, h].index_select(0, rows_t))
-        err = oracle.rel_err(got, results[h])
-        print(f"long_1m head {h} rel_err={err:.3e}")
-        assert err <= TOL["bf16"], h
+    assert not errors, errors
+    both = ErrTracker()
+    both.num = max(t.num for t in trackers.values())
+    both.den = max(t.den for t in trackers.values())
+    both.worst = max((t.worst for t in trackers.values()), key=lambda x: x[0])
+    for h in heads:
+        trackers[h].report(f"{w.name} head {h}")
+    both.report(f"{w.name} heads 0 and 63")
+    for h in heads:
+        assert trackers[h].err <= TOL["bf16"], h
+    assert both.worst[0] <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("name", ["varlen16", "varlen_short"])
-def test_varlen_workload(dev, name):
+def test_varlen_workload_all_heads(dev, name):
+    """Every head of the packed workload, checked in groups of 8 heads."""
     import torch
     w = synth.WORKLOADS[name]
     note(f"workload {w.name}")
     lengths = synth.varlen_lengths(w.batch, w.len_seed, w.len_lo, w.len_hi)
     q, k, v, cu = synth.varlen_inputs(lengths, w.heads, w.head_dim, w.dtype, w.cid, dev)
     o = _fwd(q, k, v, w.block_size, torch.from_numpy(cu).to(dev))
-    hs = [0, 21, 42, 63]
-    idx = torch.tensor(hs, device=dev)
-    sel = lambda x: host(x.index_select(0, idx))
-    ref = oracle.causal_linear_attention_varlen(sel(q), sel(k), sel(v), cu, "recurrent",
-                                                nthreads=NTHREADS)
-    err = oracle.rel_err(sel(o), ref)
-    print(f"{name} T={int(cu[-1])} rel_err={err:.3e}")
-    assert err <= TOL["bf16"]
+    tr = ErrTracker()
+    group = 8
+    for h0 in range(0, w.heads, group):
+        sl = slice(h0, min(w.heads, h0 + group))
+        ref = oracle.causal_linear_attention_varlen(host(q[sl]), host(k[sl]), host(v[sl]), cu, "recurrent",
+                                                    nthreads=NTHREADS)
+        got = host(o[sl])
+        for i in range(ref.shape[0]):
+            for s in range(len(lengths)):
+                a, b = int(cu[s]), int(cu[s + 1])
+                if b > a:
+                    tr.add(got[i, a:b], ref[i, a:b], label=f"head {h0 + i} seq {s}")
+        del ref, got
+    tr.report(f"{name} T={int(cu[-1])}")
+    assert tr.err <= TOL["bf16"]
+    assert tr.worst[0] <= TOL["bf16"]
 
 
-def test_decode256(dev):
-    """128 steps on all 256 x 64 states; sequences 0..31 (2,048 states) checked
-    in full, every step."""
+def test_decode256_every_state(dev):
+    """128 steps on all 256 x 64 states, every state and every step checked:
+    each step's o, and the states after the last step."""
     import torch
     import linear_attention_attn_amd as la
     w = synth.WORKLOADS["decode256"]
     note(f"workload {w.name}")
-    S = synth.decode_state(w.batch, w.heads, w.head_dim, w.cid, dev)
-    nchk = 32
-    S0 = host(S[:nchk]).reshape(-1, w.head_dim, w.head_dim)
+    d = w.head_dim
+    S = synth.decode_state(w.batch, w.heads, d, w.cid, dev)
+    S0 = host(S).reshape(w.batch, w.heads * d * d)      # fp32 copy of the start states
     Q, K, V, O = [], [], [], []
     for t in range(w.steps):
-        q, k, v = synth.decode_step_inputs(w.batch, w.heads, w.head_dim, w.dtype, w.cid, t, dev)
+        q, k, v = synth.decode_step_inputs(w.batch, w.heads, d, w.dtype, w.cid, t, dev)
         o = la.decode(q, k, v, S)
-        Q.append(host(q[:nchk])); K.append(host(k[:nchk])); V.append(host(v[:nchk]))
-        O.append(host(o[:nchk]))
+        # bf16 copies on the host (exact): 4 MiB per tensor and step
+        Q.append(q.cpu()); K.append(k.cpu()); V.append(v.cpu()); O.append(o.cpu())
     torch.cuda.synchronize()
-    shp = (w.steps, nchk * w.heads, w.head_dim)
-    o_ref, S_ref = oracle.decode(np.stack(Q).reshape(shp), np.stack(K).reshape(shp),
-                                 np.stack(V).reshape(shp), S0, nthreads=NTHREADS)
-    err_o = oracle.rel_err(np.stack(O).reshape(shp), o_ref)
-    err_s = oracle.rel_err(host(S[:nchk]).reshape(S_ref.shape), S_ref)
-    print(f"decode256 rel_err o={err_o:.3e} S={err_s:.3e}")
-    assert err_o <= TOL["bf16"]
-    assert err_s <= 1e-4
+    S_gpu = host(S)
+    del S
+    to32 = lambda xs, b0, b1: torch.stack([x[b0:b1] for x in xs]).float().numpy()
+    o_tr, s_tr = ErrTracker(rows=1), ErrTracker(rows=1)      # per (state, step) and per state
+    group = 64                                           # sequences per oracle call
+    for b0 in range(0, w.batch, group):
+        b1 = min(w.batch, b0 + group)
+        units = (b1 - b0) * w.heads
+        shp = (w.steps, units, d)
+        o_ref, S_ref = oracle.decode(to32(Q, b0, b1).reshape(shp), to32(K, b0, b1).reshape(shp),
+                                     to32(V, b0, b1).reshape(shp), S0[b0:b1].reshape(units, d, d),
+                                     nthreads=NTHREADS)
+        got = to32(O, b0, b1).reshape(shp)
+        for t in range(w.steps):
+            o_tr.add(got[t], o_ref[t], first_row=b0 * w.heads, label=f"step {t} (state = block)")
+        s_tr.add(S_gpu[b0:b1].reshape(units, d * d), S_ref.reshape(units, d * d), first_row=b0 * w.heads,
+                 label="final (state = block)")
+        del o_ref, S_ref, got
+    o_tr.report("decode256 o, per state and step")
+    s_tr.report("decode256 final states, per state")
+    assert o_tr.err <= TOL["bf16"]
+    assert o_tr.worst[0] <= TOL["bf16"]
+    assert s_tr.err <= 1e-4
+    assert s_tr.worst[0] <= 1e-4
