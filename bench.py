@@ -7,9 +7,12 @@ MiniMax-layer workload: batch 4, 64 heads, 8192 tokens, head_dim 128, block
 resident in HBM.  Prints ONE JSON line on stdout.
 
 Also reported in the same line (extra keys): per-kernel times from HIP events
-recorded on the library's stream, the decode step's achieved GB/s (256
-sequences x 64 heads, fp32 state, 128 steps), the 1,048,576-token prefill,
-and the CPU oracle timed on a bounded sample of the same prefill workload.
+recorded on the library's stream, the tiny fp32 case and two fp32 layer
+shapes, the decode step's achieved GB/s (256 sequences x 64 heads, fp32
+state, 128 steps), the state-handoff, rotary and indexed-decode variants, the
+1,048,576-token prefill, the packed workloads, and the CPU oracle: timed on
+the headline workload (`cpu_baseline`) and on every workload
+(`cpu_baseline_per_workload`), with the CPU model and thread count.
 """
 import argparse
 import ctypes
@@ -24,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 (vector and MFMA), TFLOP/s
 METRIC = "prefill tokens/s + TFLOP/s (% bf16 MFMA peak) at 64 heads, d=128; decode GB/s"
 
 
@@ -359,17 +363,40 @@ def copy_calibration(dev, nbytes=1 << 30, reps=5):
             "gbs_read_plus_write": 2 * nbytes / (best * 1e-3) / 1e9}
 
 
-def cpu_baseline(w, target_s):
-    """The oracle (recurrent form, fp64, OpenMP over units) on the prefill
-    workload's (sequence, head) units: the whole workload when it fits in
-    about target_s seconds (then repeated to fill them), else the largest
-    prefix of its units that does.  Scaled to tokens/s."""
+def cpu_info():
+    """The host's CPU model, the cores this process may run on and the
+    thread count the oracle uses: OMP_NUM_THREADS when it is set (the GPU
+    box sets it to the CPU share of one GPU, which a run must not exceed),
+    else every core in the affinity mask."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    try:
+        threads = min(affinity, int(omp)) if omp else affinity
+    except ValueError:
+        threads = affinity
+    return {"cpu_model": model, "cores_in_affinity": affinity, "omp_num_threads": omp,
+            "threads": max(1, threads)}
+
+
+def cpu_baseline(w, target_s, info):
+    """The oracle (recurrent form, fp64, OpenMP over units) on the headline
+    prefill workload: the whole workload, repeated to fill about target_s
+    seconds when one run is shorter (else the largest prefix of its units
+    that fits).  Scaled to tokens/s."""
     import torch
 
     import oracle
     import synth
 
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads = info["threads"]
     oracle.build(force=False)
     n, d = w.seq_len, w.head_dim
     total = w.batch * w.heads
@@ -405,7 +432,106 @@ def cpu_baseline(w, target_s):
     return {"value": tok_s, "unit": "tokens/s", "cores": min(threads, units), "kind": "oracle",
             "sample": f"recurrent fp64 form on {what} ({units} units x {n} tokens, d={d}), "
                       f"mean of {reps} run(s) of {dt:.2f} s; tokens/s = head-tokens / {w.heads} heads / time",
-            "seconds": dt * reps}
+            "seconds": dt * reps, "cpu_model": info["cpu_model"],
+            "cores_in_affinity": info["cores_in_affinity"], "omp_num_threads": info["omp_num_threads"]}
+
+
+def cpu_baseline_configs(dev, info):
+    """The oracle timed on every workload, beside the GPU figures of the same
+    run (a baseline only): the tiny fp32 case (naive and recurrent forms), the
+    MiniMax layer, the packed 16 sequences and the decode workload in full,
+    and the 1M-token prefill on heads 0 and 63 at full length (two units, so
+    two cores) with a labelled extrapolation to all 64 heads.  Inputs are the
+    workloads' own (generated on the GPU, copied to the host)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    threads = info["threads"]
+    oracle.build(force=False)
+    out = {"cpu_model": info["cpu_model"], "cores_in_affinity": info["cores_in_affinity"],
+           "omp_num_threads": info["omp_num_threads"]}
+    f32 = lambda x: x.to("cpu").to(torch.float32).numpy()
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    # tiny fp32: naive and recurrent in full
+    w = synth.WORKLOADS["tiny_f32"]
+    q, k, v = (f32(x) for x in synth.prefill_inputs(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype,
+                                                     w.cid, dev))
+    units = w.batch * w.heads
+    tn = timed(lambda: oracle.causal_linear_attention(q, k, v, "naive", nthreads=threads))
+    tr = timed(lambda: oracle.causal_linear_attention(q, k, v, "recurrent", nthreads=threads))
+    out["tiny_f32"] = {"sample": "whole workload", "threads": min(threads, units),
+                       "naive_s": tn, "recurrent_s": tr,
+                       "tokens_per_s_recurrent": w.batch * w.seq_len / tr}
+    log(json.dumps({"cpu tiny_f32": out["tiny_f32"]}))
+
+    # MiniMax layer in full
+    w = synth.WORKLOADS["minimax_layer"]
+    q, k, v = (f32(x) for x in synth.prefill_inputs(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype,
+                                                     w.cid, dev))
+    t = timed(lambda: oracle.causal_linear_attention(q, k, v, "recurrent", nthreads=threads))
+    out["minimax_layer"] = {"sample": "whole workload", "threads": min(threads, w.batch * w.heads),
+                            "seconds": t, "tokens_per_s": w.batch * w.seq_len / t}
+    del q, k, v
+    log(json.dumps({"cpu minimax_layer": out["minimax_layer"]}))
+
+    # 1M tokens: heads 0 and 63 at full length, one core each
+    w = synth.WORKLOADS["long_1m"]
+    q, k, v = (f32(x)[0] for x in synth.prefill_inputs(w.batch, w.heads, w.seq_len, w.head_dim, w.dtype,
+                                                        w.cid, dev, heads_subset=[0, 63]))
+    t = timed(lambda: oracle.causal_linear_attention(q, k, v, "recurrent", nthreads=min(2, threads)))
+    ht = 2 * w.seq_len / t
+    out["long_1m"] = {"sample": "heads 0 and 63 at full length (2 units on 2 cores)",
+                      "threads": min(2, threads), "seconds": t, "head_tokens_per_s": ht,
+                      "extrapolated_tokens_per_s_all_heads": ht / w.heads * min(threads, w.heads) / 2,
+                      "extrapolation": f"EXTRAPOLATED, not measured: head-token rate of the 2 measured "
+                                       f"units x {min(threads, w.heads)} / 2 cores (all {w.heads} heads "
+                                       f"as independent units on {min(threads, w.heads)} threads), "
+                                       f"/ {w.heads} heads per token"}
+    del q, k, v
+    log(json.dumps({"cpu long_1m": out["long_1m"]}))
+
+    # packed 16 sequences in full, in groups of 8 heads (host memory)
+    w = synth.WORKLOADS["varlen16"]
+    lengths = synth.varlen_lengths(w.batch, w.len_seed, w.len_lo, w.len_hi)
+    tot = 0.0
+    T = int(synth.cu_from_lengths(lengths)[-1])
+    for h0 in range(0, w.heads, 8):
+        hs = list(range(h0, min(w.heads, h0 + 8)))
+        q, k, v, cu = synth.varlen_inputs(lengths, w.heads, w.head_dim, w.dtype, w.cid, dev, heads_subset=hs)
+        q, k, v = f32(q), f32(k), f32(v)
+        tot += timed(lambda: oracle.causal_linear_attention_varlen(q, k, v, cu, "recurrent", nthreads=threads))
+        del q, k, v
+    out["varlen16"] = {"sample": f"whole workload ({T} tokens x {w.heads} heads, 8 heads per call)",
+                       "threads": threads, "seconds": tot, "tokens_per_s": T / tot}
+    log(json.dumps({"cpu varlen16": out["varlen16"]}))
+
+    # decode: every state, all steps
+    w = synth.WORKLOADS["decode256"]
+    S0 = synth.decode_state(w.batch, w.heads, w.head_dim, w.cid, dev).cpu().numpy()
+    units = w.batch * w.heads
+    qs, ks, vs = [], [], []
+    for t_ in range(w.steps):
+        a, b, c = synth.decode_step_inputs(w.batch, w.heads, w.head_dim, w.dtype, w.cid, t_, dev)
+        qs.append(f32(a).reshape(units, -1)); ks.append(f32(b).reshape(units, -1))
+        vs.append(f32(c).reshape(units, -1))
+    Q, K, V = np.stack(qs), np.stack(ks), np.stack(vs)
+    del qs, ks, vs
+    t = timed(lambda: oracle.decode(Q, K, V, S0.reshape(units, w.head_dim, w.head_dim), nthreads=threads))
+    d = w.head_dim
+    out["decode256"] = {"sample": f"whole workload ({units} states x {w.steps} steps)", "threads": threads,
+                        "seconds": t, "ms_per_step": t * 1e3 / w.steps,
+                        "gbs_algorithmic": units * w.steps * (8 * d * d + 8 * d) / t / 1e9}
+    log(json.dumps({"cpu decode256": out["decode256"]}))
+    del Q, K, V, S0
+    return out
 
 
 def main():
@@ -423,8 +549,11 @@ def main():
                     help="only the decode workload (one line with its figures; for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--workload", default="minimax_layer",
-                    choices=["minimax_layer", "long_1m", "tiny_f32"],
+                    choices=["minimax_layer", "long_1m", "tiny_f32", "minimax_layer_f32", "layer_f32_d64",
+                             "varlen16", "varlen_short"],
                     help="dense prefill workload of the headline line")
+    ap.add_argument("--calibrate-only", action="store_true",
+                    help="only the plain 1 GiB device copy (for the byte-counter calibration)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also time a plain 1 GiB device copy (the reference kernel for the "
                          "HBM byte counters) and report its GB/s")
@@ -441,6 +570,11 @@ def main():
 
     la.load_library()
     dev = torch.device("cuda:0")
+    if args.calibrate_only:
+        # the plain device copy alone (the reference kernel for the HBM byte
+        # counters), in a process of its own
+        print(json.dumps({"copy_calibration": copy_calibration(dev)}), flush=True)
+        return
     if args.decode_only:
         wd = synth.WORKLOADS["decode256"]
         dms, dgbs, dtok = bench_decode(wd, 1, dev)
@@ -449,6 +583,15 @@ def main():
               flush=True)
         return
     w = synth.WORKLOADS[args.workload]
+    if w.kind == "varlen":
+        # one packed workload on its own (for profiling runs): one line with its figures
+        vms, vstage, vchunk, vT = bench_prefill_varlen(w, args.steps, args.warmup, dev)
+        vbytes = w.heads * vT * 4 * w.head_dim * 2
+        print(json.dumps({w.name: {"workload": w.note, "tokens": vT, "ms_per_step": vms,
+                                   "hbm_gbs": vbytes / (vms * 1e-3) / 1e9,
+                                   "roofline_frac": vbytes / (PEAK_HBM_GBS * 1e9) / (vms * 1e-3),
+                                   "kernels_ms": vstage, "chunk_tokens": vchunk}}), flush=True)
+        return
     d, B = w.head_dim, w.block_size
     head_tokens = w.batch * w.heads * w.seq_len
     tokens = w.batch * w.seq_len
@@ -492,6 +635,28 @@ def main():
     log(json.dumps({k: out[k] for k in ("value", "ms_per_step", "tflops", "kernels_ms")}))
 
     if not args.no_extras:
+        for tname, tsteps, twarm in (("tiny_f32", 200, 50), ("minimax_layer_f32", 10, 5),
+                                     ("layer_f32_d64", 20, 10)):
+            wt = synth.WORKLOADS[tname]
+            log(f"prefill {wt.name}: {wt.note}")
+            tms, tstage, tchunk, _ = bench_prefill(wt, tsteps, twarm, dev)
+            tht = wt.batch * wt.heads * wt.seq_len
+            tbytes = tht * 4 * wt.head_dim * 4
+            tfl = tht * prefill_flops_per_head_token(wt.head_dim, wt.block_size)
+            fused_s = tstage["fused"] * 1e-3
+            out[tname] = {"workload": wt.note, "ms_per_step": tms,
+                          "tokens_per_s": wt.batch * wt.seq_len / (tms * 1e-3),
+                          "hbm_gbs": tbytes / (tms * 1e-3) / 1e9,
+                          "tflops": tfl / (tms * 1e-3) / 1e12,
+                          "kernels_ms": tstage, "chunk_tokens": tchunk,
+                          "fused_hbm_frac": tbytes / fused_s / 1e9 / PEAK_HBM_GBS,
+                          "fused_fp32_mfma_frac": tfl / fused_s / 1e12 / PEAK_FP32_TFLOPS,
+                          "roofline_frac_step": max(tfl / (PEAK_FP32_TFLOPS * 1e12),
+                                                    tbytes / (PEAK_HBM_GBS * 1e9)) / (tms * 1e-3)}
+            if tname == "tiny_f32":
+                out[tname]["note"] = ("correctness-size case: 2 MB of traffic (0.26 us at 8 TB/s), bound by "
+                                      "kernel launch latency")
+            log(json.dumps(out[tname]))
         wd = synth.WORKLOADS["decode256"]
         log(f"decode {wd.name}: {wd.note}")
         dms, dgbs, dtok = bench_decode(wd, 5, dev)
@@ -554,9 +719,12 @@ def main():
         log(json.dumps(out["copy_calibration"]))
 
     if not args.no_cpu:
-        log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        info = cpu_info()
+        log("cpu baseline (oracle)", json.dumps(info))
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, info)
         log(json.dumps(out["cpu_baseline"]))
+        if not args.no_extras:
+            out["cpu_baseline_per_workload"] = cpu_baseline_configs(dev, info)
     print(json.dumps(out), flush=True)
 
 
