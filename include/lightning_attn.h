@@ -44,6 +44,8 @@ extern "C" {
 #define LA_EUNSUPPORTED 2  /* head_dim not 64/128, block_size not 64/128/256, or dtype unknown */
 #define LA_EWORKSPACE   3  /* workspace NULL or smaller than the size query returned */
 #define LA_EHIP         4  /* a HIP launch failed; see hipGetLastError semantics     */
+#define LA_ESCRATCH     5  /* lightning_attn_fwd_noalloc: the call needs more scratch than
+                              LA_NOALLOC_SCRATCH_BYTES */
 
 /*
  * Bytes of device workspace lightning_attn_fwd needs for these arguments
@@ -289,6 +291,27 @@ int lightning_attn_fwd_planned(const void *q, const void *k, const void *v, void
                                int rope_dims, double rope_base, const int32_t *pos_offset,
                                int64_t chunk_tokens, int64_t sub_tokens,
                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * lightning_attn_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels, arguments, layouts, checks and results as
+ * lightning_attn_fwd, without the workspace arguments.  The scratch the
+ * kernels need (chunk tables and per-sub-chunk fp32 states) lives in a
+ * static device array of LA_NOALLOC_SCRATCH_BYTES that each GPU the library
+ * runs on holds until the process ends; the call allocates nothing.
+ * A call whose lightning_attn_fwd_workspace_size(...) exceeds
+ * LA_NOALLOC_SCRATCH_BYTES returns LA_ESCRATCH before any launch (e.g. 64
+ * heads x 1,048,576 tokens needs more; the MiniMax layer and packed inputs
+ * of a few hundred thousand tokens fit).  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (other streams, other threads)
+ * race and must be ordered by the caller.  Nothing in the array needs
+ * clearing between calls: the kernels write every table and state they read.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int lightning_attn_fwd_noalloc(const void *q, const void *k, const void *v, void *o,
+                               int batch, int heads, int64_t seq_len, int head_dim, int block_size,
+                               const int32_t *cu_seqlens, int dtype, void *stream);
 
 /* Static, human-readable text for a status code. */
 const char *lightning_attn_strerror(int status);

@@ -25,12 +25,14 @@ __all__ = [
     "decode", "LA_FWD_NUM_EVENTS", "lightning_attn_fwd_state", "lightning_attn_fwd_rope",
     "lightning_attn_decode_indexed", "lightning_attn_decode_rope", "decode_indexed", "decode_rope",
     "lightning_attn_fwd_indexed", "lightning_attn_fwd_workspace_size_planned",
-    "lightning_attn_fwd_planned",
+    "lightning_attn_fwd_planned", "lightning_attn_fwd_noalloc", "LA_ESCRATCH",
+    "LA_NOALLOC_SCRATCH_BYTES",
 ]
 
 LA_DTYPE_BF16 = 0
 LA_DTYPE_F32 = 1
-LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EWORKSPACE, LA_EHIP = 0, 1, 2, 3, 4
+LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EWORKSPACE, LA_EHIP, LA_ESCRATCH = 0, 1, 2, 3, 4, 5
+LA_NOALLOC_SCRATCH_BYTES = 128 << 20
 LA_FWD_NUM_EVENTS = 5
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -88,6 +90,8 @@ def load_library():
     lib.lightning_attn_fwd_planned.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, i32, vp, vp,
                                                vp, i32, vp, i32, ctypes.c_double, vp, i64, i64, vp, sz, vp]
     lib.lightning_attn_fwd_planned.restype = i32
+    lib.lightning_attn_fwd_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, vp, i32, vp]
+    lib.lightning_attn_fwd_noalloc.restype = i32
     lib.lightning_attn_strerror.argtypes = [i32]
     lib.lightning_attn_strerror.restype = ctypes.c_char_p
     _LIB = lib
@@ -163,6 +167,13 @@ def lightning_attn_fwd_planned(q, k, v, o, batch, heads, seq_len, head_dim, bloc
         _ptr(cu_seqlens), dtype, _ptr(s_init), _ptr(s_final), _ptr(state_pool), nslots, _ptr(slots),
         rope_dims, float(rope_base), _ptr(pos_offset), chunk_tokens, sub_tokens, _ptr(workspace),
         workspace_bytes, stream))
+
+
+def lightning_attn_fwd_noalloc(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens,
+                               dtype, stream) -> int:
+    return int(load_library().lightning_attn_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, heads, seq_len, head_dim, block_size,
+        _ptr(cu_seqlens), dtype, stream))
 
 
 def lightning_attn_fwd_traced(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens,

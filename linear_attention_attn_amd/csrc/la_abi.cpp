@@ -387,6 +387,7 @@ const char *lightning_attn_strerror(int status) {
         case LA_EUNSUPPORTED: return "unsupported head_dim, block_size, dtype or size";
         case LA_EWORKSPACE: return "workspace missing or smaller than lightning_attn_fwd_workspace_size()";
         case LA_EHIP: return "HIP kernel launch failed";
+        case LA_ESCRATCH: return "the call needs more scratch than the allocation-free entry point holds";
         default: return "unknown status";
     }
 }

@@ -214,6 +214,18 @@ def test_no_plan_knobs_in_environment(monkeypatch, la):
             assert knob not in txt, (f, knob)
 
 
+def test_noalloc_refuses_on_the_host(la):
+    """The allocation-free entry point refuses a call whose scratch would not
+    fit its static array, and bad shapes, before touching the GPU."""
+    fake = 1 << 20
+    assert la.lightning_attn_fwd_workspace_size(1, 64, 1 << 20, 128, 256, 0, 0) > la.LA_NOALLOC_SCRATCH_BYTES
+    assert la.lightning_attn_fwd_noalloc(fake, fake, fake, fake, 1, 64, 1 << 20, 128, 256, None, 0,
+                                         None) == la.LA_ESCRATCH
+    assert la.lightning_attn_fwd_noalloc(fake, fake, fake, fake, 1, 1, 10, 96, 256, None, 0, None) == 2
+    assert la.lightning_attn_fwd_noalloc(None, None, None, None, 1, 1, 0, 128, 256, None, 0, None) == 0
+    assert la.lightning_attn_strerror(la.LA_ESCRATCH) != "unknown status"
+
+
 def test_product_never_imports_oracle():
     """The HIP path must not route through the CPU oracle."""
     pkg = os.path.join(ROOT, "linear_attention_attn_amd")
