@@ -1456,6 +1456,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         // a chunk that starts from zero has Q S = 0 in its first block
         bool zero_s = false;
         if constexpr (first && J < TPB) zero_s = zs && sb == 0;
+        // (one slab per wave: a slab starting past the chunk end has no output)
+        if constexpr (first && C::NSW == 1) zero_s = zero_s || 16 * slab_of<BLK, NW>(w, 0) >= n - tb;
         if (zero_s) {
 #pragma unroll
             for (int si = 0; si < C::NSW; ++si)
@@ -1497,8 +1499,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
 #pragma unroll
             for (int si = 0; si < C::NSW; ++si) {
                 const int i0 = 16 * slab_of<BLK, NW>(w, si);
-                need[si] = jb <= i0 + 15;
-                need1[si] = jb + 16 <= i0 + 15;
+                // last key the slab sees: keys past the chunk end add nothing,
+                // and a slab starting past it has no output (-1: skip all)
+                const int left = n - tb;
+                const int kmax = i0 < left ? min(i0 + 15, left - 1) : -1;
+                need[si] = jb <= kmax;
+                need1[si] = jb + 16 <= kmax;
                 P[si][0] = zero4();
                 P[si][1] = zero4();
             }
@@ -1576,7 +1582,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
 
         if constexpr (last) {
             if constexpr (TPB == 1) load_q(Q, tb + BLK, 0, C::KC);   // this block's Q is dead after its scores
-            if (more || fdst) state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
+            if ((more || fdst) && jt * TJ < n - tb) state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
             if (more) {
                 if constexpr (first) {               // one-tile blocks: the state copy was read in this tile
                     wait_vm_lgkm0<63>();
@@ -1603,7 +1609,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
             if constexpr (LA > 1) issue(t + LA, stages[(J + LA) % NST]);
             if constexpr (ROPE) wait_vm_lgkm0<63>();     // the rotated tile is written
         } else {
-            if (more || fdst) state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
+            if ((more || fdst) && jt * TJ < n - tb) state_update_tr<TJ, C::SA, C::SB>(S, ka, vbs);
             // DMA(t+1) has landed; younger are DMA(t+2 .. t+LA) and the Q
             // loads of the LA-1 tiles up to this one
             wait_vm_lgkm0<(LA - 1) * IPW + (LA >= 2 ? QS::n(jt) : 0) + (LA >= 3 ? QS::n(jt - 1) : 0)>();
@@ -1612,11 +1618,22 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
         wg_barrier();
     };
 
+    // Tiles past the chunk's last token hold only zeros: with blocks of two
+    // or more tiles the walk stops after the last tile with tokens
+    // (wave-uniform).  Every wave with rows in the chunk has stored its O by
+    // then, since a 16-row slab never straddles a tile; the rest of the block
+    // would only add zeros to the state.  (With one tile per block the
+    // compiler drains the whole load queue at such exits, so that walk keeps
+    // its padding blocks.)
     static_assert(NST == 4, "ring stages");
+    const int ntile = TPB > 1 ? (n + TJ - 1) / TJ : nsb * NST;
     for (int sb = 0; sb < nsb; ++sb) {
         tile(integral_constant<int, 0>{}, sb);
+        if (TPB > 1 && sb * NST + 1 >= ntile) break;
         tile(integral_constant<int, 1>{}, sb);
+        if (TPB > 1 && sb * NST + 2 >= ntile) break;
         tile(integral_constant<int, 2>{}, sb);
+        if (TPB > 1 && sb * NST + 3 >= ntile) break;
         tile(integral_constant<int, 3>{}, sb);
     }
     wait_vm_lgkm0<0>();                              // DMA past the chunk end and the stores are done

@@ -96,6 +96,44 @@ def test_integer_exact(dev, dt, d, B, n, C, S):
     assert np.array_equal(o.astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B", [128, 256])
+@pytest.mark.parametrize("C", [0, 512])
+def test_partial_last_block_exact(dev, d, B, C):
+    """Sequences ending on both sides of every 16-row slab and 64-token tile
+    edge inside their last block, where the kernel skips the slabs and keys
+    past the end and stops after the last tile with tokens: integer-exact
+    inputs, so o and the final states must equal the oracle bit for bit;
+    dense (one length per call) and packed (all lengths in one call), with
+    one chunk per sequence (C = 0) and with chunks of 512 tokens."""
+    import torch
+    import linear_attention_attn_amd as la
+    ends = [1, 15, 16, 17, 63, 64, 65, 127, 129, 191, 192, 193, B - 1]
+    lengths = [e for e in ends if e < B] + [B + 47, 2 * B + 80, 3 * B - 1]
+    rng = np.random.default_rng(d + B + C)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
+    H = 2
+    with chunk_tokens(C):
+        for n in lengths:
+            note(f"partial last block dense d={d} B={B} C={C} n={n}")
+            qh, kh, vh = _onehot_inputs(rng, (1, H, n, d))
+            Sf = torch.full((1, H, d, d), float("nan"), device=dev)
+            o = host(la.fwd(t(qh), t(kh), t(vh), block_size=B, s_final=Sf))
+            ref, sref = oracle.causal_linear_attention_state(qh, kh, vh)
+            assert np.array_equal(o.astype(np.float64), ref), n
+            assert np.array_equal(host(Sf).astype(np.float64), sref), n
+        note(f"partial last block packed d={d} B={B} C={C}")
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+        T = int(cu[-1])
+        qh, kh, vh = _onehot_inputs(rng, (H, T, d))
+        Sf = torch.full((len(lengths), H, d, d), float("nan"), device=dev)
+        o = host(la.fwd(t(qh), t(kh), t(vh), block_size=B, cu_seqlens=torch.from_numpy(cu).to(dev),
+                        s_final=Sf))
+        ref, sref = oracle.causal_linear_attention_varlen_state(qh, kh, vh, cu)
+        assert np.array_equal(o.astype(np.float64), ref)
+        assert np.array_equal(host(Sf).astype(np.float64), sref)
+
+
 def test_one_hot_boundaries(dev):
     """k_{j0} = e_a, v_{j0} = e_c, q_i = e_a: o_i = [i >= j0] e_c, at block and
     chunk edges."""
