@@ -963,6 +963,280 @@ struct Ring<2, SBY> {
 };
 
 
+// ------------------------------------------------------ k_fused_ring (fp32)
+// fp32 with d = 64 (no rotary prologue): k_fused's products over K/V tiles
+// that stream through a 4-stage ring of row-major LDS tiles, filled by
+// buffer-to-LDS loads three tiles ahead (48 KiB in flight instead of the one
+// register-staged tile of k_fused).  Rows are stored with LdsRows' swizzle
+// (each lane's global source offset is permuted accordingly), so a stage's
+// K tile is itself the row-major operand of the scores.  The products that
+// reduce over tokens read transposed tiles: at the top of tile t the patch
+// threads transpose tile t + 1 into the second half of its own stage, which
+// the barrier at the end of tile t publishes; one barrier per tile.  Every
+// tile, loaded or transposed, lives in its compile-time ring stage, so the
+// compiler keeps its buffer-to-LDS loads apart and waits only for what a read
+// needs.  All global accesses of K and V go through buffer resources that
+// end at the chunk end, so tiles past it load as zeros.
+template <int BLK>
+__global__ __launch_bounds__(512, 1) void k_fused_ring(KParams p) {
+    using T = float;
+    constexpr int D = 64;
+    using C = Cfg<T, D, BLK>;
+    constexpr int TJ = C::TJ;                        // 32 tokens per tile
+    constexpr int TPB = BLK / TJ;                    // tiles per block (2, 4, 8)
+    constexpr int NST = 4, LA = 3;                   // ring stages; tiles requested ahead
+    constexpr int RB = D * 4;                        // bytes per token row
+    constexpr int TB = TJ * RB;                      // bytes of one tensor tile
+    constexpr int SBY = 2 * TB + 2 * C::KT_BYTES;    // stage: K, V tiles, then their transposes
+    constexpr int NI = TB / 1024;                    // 1 KiB loads per tensor tile
+    constexpr int IPW = 2 * NI / C::NW;              // loads per wave per tile
+    static_assert(C::NW == 8 && IPW == 2 && C::KR_ROW == RB && TPB >= 2, "tile split");
+    __shared__ __attribute__((aligned(16))) char st[C::ST_BYTES];
+    char *stages[NST];
+    Ring<NST, SBY>::get(stages);
+
+    int h, s;
+    int64_t gch;
+    if (!chunk_of_block(p, h, gch, s)) return;
+    const Unit u = unit_of<D>(p, s, h);
+    const int64_t cl = gch - p.chunk_off[s];
+    const int64_t t0 = cl * p.chunk;
+    const int n = (int)min(u.len - t0, p.chunk);     // tokens of this chunk
+    const int64_t t1 = t0 + n;
+    const int64_t cb = (u.base + t0 * D) * 4;        // byte offset of its first row
+    const uint32_t nbytes = (uint32_t)n * RB;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const char *>(p.k) + cb, nbytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const char *>(p.v) + cb, nbytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(static_cast<char *>(p.o) + cb, nbytes);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const char *>(p.q) + cb, nbytes);
+
+    const int w = wave_id(), l = lane_id(), c = l & 15, g = l >> 4;
+    const int a0 = C::SA * (w % C::AW), b0 = C::SB * (w / C::AW);
+    const int ct0 = C::CSPLIT == 1 ? 0 : (w >> 2) * C::NCT;
+    const int nblk = (n + BLK - 1) / BLK;
+    const int ntile = (n + TJ - 1) / TJ;             // tiles holding tokens
+    const int nsb = (ntile + NST - 1) / NST;
+
+    // loads: wave instruction gi = w * IPW + ii fills rows 4x .. 4x + 3 of the
+    // K (gi < NI) or V tile, x = gi mod NI; lane l brings row 4x + l / 16,
+    // the 16-byte chunk that lands at physical chunk l % 16 of the row
+    uint32_t dvo[IPW], dlo[IPW];
+    __amdgpu_buffer_rsrc_t drs[IPW];
+#pragma unroll
+    for (int ii = 0; ii < IPW; ++ii) {
+        const int gi = w * IPW + ii;
+        const bool isv = gi >= NI;
+        const int row = 4 * (isv ? gi - NI : gi) + (l >> 4);
+        dvo[ii] = (uint32_t)(row * RB + (((l & 15) ^ LdsRows<RB>::swz(row)) << 4));
+        dlo[ii] = (isv ? TB : 0) + 1024 * (isv ? gi - NI : gi);
+        drs[ii] = isv ? rv : rk;
+    }
+    auto issue = [&](int tile, char *stage) {
+#pragma unroll
+        for (int ii = 0; ii < IPW; ++ii) dma_lds16(drs[ii], stage + dlo[ii], dvo[ii], (uint32_t)(tile * TB));
+    };
+    // transposed copy of a stage's tiles: the patch threads read their
+    // 4-token x 16-byte patch of K or V from the stage and write it transposed
+    // into the stage's second half
+    auto transpose = [&](char *stage) {
+        char *tbuf = stage + 2 * TB;
+        const int t = threadIdx.x;
+        const bool isk = t < C::NP, isv = t >= 256 && t < 256 + C::NP;
+        if (!isk && !isv) return;
+        const int pi = isk ? t : t - 256;
+        const int tg = pi / (D / C::EPC), ch = pi % (D / C::EPC);
+        const char *src = stage + (isk ? 0 : TB);
+        Patch<T, D> pt;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            pt.x[r] = *reinterpret_cast<const u32x4_t *>(src + LdsRows<RB>::off(4 * tg + r, ch * 16));
+        patch_store<T, D, BLK, false>(pt, nullptr, tbuf, tbuf + C::KT_BYTES);
+    };
+
+    // ---- state at the chunk start
+    f32x4_t S[C::SA][C::SB];
+    float *const fdst = final_state_dst<D>(p, s, h, gch);
+    {
+        const float *src = chunk_start_state<D>(p, s, h, cl);
+#pragma unroll
+        for (int ia = 0; ia < C::SA; ++ia)
+#pragma unroll
+            for (int ib = 0; ib < C::SB; ++ib)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    S[ia][ib][r] = src ? src[((a0 + ia) * 16 + 4 * g + r) * D + (b0 + ib) * 16 + c] : 0.f;
+#pragma unroll
+        for (int ia = 0; ia < C::SA; ++ia)
+#pragma unroll
+            for (int ib = 0; ib < C::SB; ++ib)
+                lds_write4<T, C::ST_ROW>(st, (b0 + ib) * 16 + c, (a0 + ia) * 16 + 4 * g, S[ia][ib]);
+    }
+    // Q fragments of this wave's row slabs: row 16*slab + c, d = 32*kc + 8g .. +7,
+    // by buffer loads that are always issued (rows past the chunk end read as
+    // zeros), so the explicit waits below can count them
+    Frag<T> Q[C::NSW][C::KC];
+    constexpr int QL = 2 * C::NSW * C::KC;           // Q loads per wave per block
+    auto load_q = [&](int brow) {                    // the block's first row in the chunk
+#pragma unroll
+        for (int si = 0; si < C::NSW; ++si) {
+            const uint32_t voff = (uint32_t)((brow + 16 * slab_of<BLK>(w, si) + c) * RB + 8 * g * 4);
+#pragma unroll
+            for (int kc = 0; kc < C::KC; ++kc) {
+                const f32x4_t x0 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)voff + kc * 128, 0, 0));
+                const f32x4_t x1 = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)voff + kc * 128 + 16, 0, 0));
+#pragma unroll
+                for (int m = 0; m < 4; ++m) { Q[si][kc].f[m] = x0[m]; Q[si][kc].f[4 + m] = x1[m]; }
+            }
+        }
+    };
+    load_q(0);
+    issue(0, stages[0]);
+    issue(1, stages[1]);
+    issue(2, stages[2]);
+    wait_vm_lgkm0<IPW>();                            // the first two tiles (and Q) have landed
+    wg_barrier();
+    transpose(stages[0]);
+    wait_vm_lgkm0<IPW>();
+    wg_barrier();
+
+    f32x4_t O[C::NSW][C::NCT];
+    using std::integral_constant;
+    auto tile = [&](auto J_c, int sb) {
+        constexpr int J = decltype(J_c)::value;     // ring stage of the tile
+        const int t = sb * NST + J;
+        const int bi = t / TPB, jt = t % TPB;
+        const int64_t tb = t0 + (int64_t)bi * BLK;   // the block's first token
+        const bool more = bi + 1 < nblk;
+        const bool block_end = jt == TPB - 1 || t + 1 >= ntile;
+        issue(t + LA, stages[(J + LA) % NST]);
+        // the next tile has landed (waited for before the barrier that ended
+        // the previous tile): its transposed copy, published by this tile's
+        // barrier
+        transpose(stages[(J + 1) % NST]);
+        const char *kr = stages[J];
+        const char *kt = stages[J] + 2 * TB;
+        const char *vt = kt + C::KT_BYTES;
+
+        if (jt == 0) {
+            // ---- inter-block right product with the block-start state: O^T = S^T Q^T
+#pragma unroll
+            for (int si = 0; si < C::NSW; ++si)
+#pragma unroll
+                for (int ct = 0; ct < C::NCT; ++ct) O[si][ct] = zero4();
+#pragma unroll
+            for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+                for (int kc = 0; kc < C::KC; ++kc) {
+                    const Frag<T> A = lds_read8<T, C::ST_ROW>(st, (ct0 + ct) * 16 + c, kc * 32 + 8 * g);
+#pragma unroll
+                    for (int si = 0; si < C::NSW; ++si) mma(O[si][ct], A, Q[si][kc]);
+                }
+        }
+        // ---- intra-block left product for this K/V tile (keys jt*TJ .. of the block)
+        const int left = (int)(t1 - tb);             // tokens of the chunk from this block on
+        {
+            const int jb = jt * TJ;
+            f32x4_t P[C::NSW][2];
+            bool need[C::NSW], need1[C::NSW];
+#pragma unroll
+            for (int si = 0; si < C::NSW; ++si) {
+                const int i0 = 16 * slab_of<BLK>(w, si);
+                const int kmax = i0 < left ? min(i0 + 15, left - 1) : -1;   // last key the slab sees
+                need[si] = jb <= kmax;
+                need1[si] = jb + 16 <= kmax;
+                P[si][0] = zero4();
+                P[si][1] = zero4();
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                bool any = false;
+#pragma unroll
+                for (int si = 0; si < C::NSW; ++si) any |= hh ? need1[si] : need[si];
+                if (!any) continue;
+#pragma unroll
+                for (int kc = 0; kc < C::KC; ++kc) {
+                    const Frag<T> A = lds_read8<T, C::KR_ROW>(kr, 16 * hh + c, kc * 32 + 8 * g);
+#pragma unroll
+                    for (int si = 0; si < C::NSW; ++si)
+                        if (hh ? need1[si] : need[si]) mma(P[si][hh], A, Q[si][kc]);
+                }
+            }
+            Frag<T> PF[C::NSW];
+#pragma unroll
+            for (int si = 0; si < C::NSW; ++si) {
+                const int i0 = 16 * slab_of<BLK>(w, si);
+                const int i = i0 + c;                  // block-local query row
+                if (need[si] && jb + 31 > i0) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (jb + 4 * g + r > i) P[si][0][r] = 0.f;
+                        if (jb + 16 + 4 * g + r > i) P[si][1][r] = 0.f;
+                    }
+                }
+                PF[si] = frag_from_f32(P[si][0], P[si][1], T{});
+            }
+            bool anyg = false;
+#pragma unroll
+            for (int si = 0; si < C::NSW; ++si) anyg |= need[si];
+            if (anyg) {
+#pragma unroll
+                for (int ct = 0; ct < C::NCT; ++ct) {
+                    const Frag<T> A = lds_read4x2<T, C::KT_ROW>(vt, (ct0 + ct) * 16 + c, 4 * g, 16 + 4 * g);
+#pragma unroll
+                    for (int si = 0; si < C::NSW; ++si)
+                        if (need[si]) mma(O[si][ct], A, PF[si]);
+                }
+            }
+        }
+        // this block's Q is dead after its last tile's scores: fetch the next block's
+        const bool q_next = block_end && more;
+        if (q_next) load_q((bi + 1) * BLK);
+        // ---- state for the next block
+        if (more || fdst) state_update<T, D, BLK, C::SA, C::SB>(S, kt, vt, a0, b0);
+        if (block_end) {
+            // ---- store O: lane holds row (16*slab + c), columns 16*ct + 4g .. +3
+            // (buffer stores from inline asm, outside the compiler's count of
+            // outstanding loads; rows past the chunk end are dropped)
+#pragma unroll
+            for (int si = 0; si < C::NSW; ++si) {
+                const uint32_t row = (uint32_t)(bi * BLK + 16 * slab_of<BLK>(w, si) + c);
+#pragma unroll
+                for (int ct = 0; ct < C::NCT; ++ct)
+                    store16(ro, row * RB + ((ct0 + ct) * 16 + 4 * g) * 4, __builtin_bit_cast(u32x4_t, O[si][ct]));
+            }
+            // the block-start state copy for the next block: every wave read the
+            // old one in the block's first tile, before a barrier
+            if (more) {
+#pragma unroll
+                for (int ia = 0; ia < C::SA; ++ia)
+#pragma unroll
+                    for (int ib = 0; ib < C::SB; ++ib)
+                        lds_write4<T, C::ST_ROW>(st, (b0 + ib) * 16 + c, (a0 + ia) * 16 + 4 * g, S[ia][ib]);
+            }
+        }
+        // the tile after next has landed: younger are the loads of tile t + 3
+        // and the next block's Q (the stores, when younger, only make the
+        // wait stricter)
+        if (q_next) wait_vm_lgkm0<IPW + QL>();
+        else wait_vm_lgkm0<IPW>();
+        wg_barrier();
+    };
+
+    // tiles past the chunk's last token hold only zeros: the walk stops
+    // after the last tile with tokens (every block's O is stored there)
+    for (int sb = 0; sb < nsb; ++sb) {
+        tile(integral_constant<int, 0>{}, sb);
+        if (sb * NST + 1 >= ntile) break;
+        tile(integral_constant<int, 1>{}, sb);
+        if (sb * NST + 2 >= ntile) break;
+        tile(integral_constant<int, 2>{}, sb);
+        if (sb * NST + 3 >= ntile) break;
+        tile(integral_constant<int, 3>{}, sb);
+    }
+    wait_vm_lgkm0<0>();                              // loads past the chunk end and the stores are done
+    if (fdst) store_state<D, C::SA, C::SB>(fdst, S, a0, b0, c, g);
+}
+
 // The 1 KiB piece filled by wave instruction gi (IPW per wave, NI pieces
 // per tensor tile, RGN 16-row groups per tile): 16 rows (row0..) of the
 // 32-element column block blk of the K (gi < NI) or V tile.  With ROPE the
@@ -1688,6 +1962,8 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
         constexpr int NWF = fused_waves(D, BLK);
         hipLaunchKernelGGL((k_fused_dma<D, BLK, NWF, 64, 4, 2, ROPE>), gchunks, dim3(NWF * 64), 0, st, kp);
     }
+    else if constexpr (D == 64 && !ROPE)
+        hipLaunchKernelGGL((k_fused_ring<BLK>), gchunks, dim3(512), 0, st, kp);
     else
         hipLaunchKernelGGL((k_fused<T, D, BLK, ROPE>), gchunks, dim3(512), 0, st, kp);
     mark(4);

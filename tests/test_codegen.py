@@ -75,7 +75,7 @@ def test_hazard_scan_catches_pattern():
 
 def test_bf16_prefill_kernels_do_not_spill(tmp_path):
     text = _asm(os.path.join(CSRC, "la_prefill.hip"), tmp_path)
-    kernels = re.findall(r"^(_ZN2la1\dk_(?:fused_dma|summary_reg)\w+):", text, re.M)
+    kernels = re.findall(r"^(_ZN2la1\dk_(?:fused_dma|fused_ring|summary_reg)\w+):", text, re.M)
     assert kernels
     for k in kernels:
         i = text.index(k + ":")
@@ -101,4 +101,19 @@ def test_fused_kernel_keeps_prefetch_in_flight(tmp_path):
         # kernel waits for everything; nothing else may drain the queue
         full = [s for s in insts if re.fullmatch(r"s_waitcnt vmcnt\(0\)", s)]
         assert len(full) <= 1, (k, len(full))
+    assert found
+
+
+def test_fp32_ring_kernel_keeps_prefetch_in_flight(tmp_path):
+    """The fp32 ring kernel waits for everything only in its prologue (the
+    chunk's start state and first Q, before its first barrier) and at its
+    end."""
+    text = _asm(os.path.join(CSRC, "la_prefill.hip"), tmp_path)
+    found = False
+    for k, body in _kernel_bodies(text, r"^(_ZN2la12k_fused_ring\w+):"):
+        found = True
+        insts = list(_instructions(body))
+        first_barrier = next(i for i, s in enumerate(insts) if s == "s_barrier")
+        late = [s for s in insts[first_barrier:] if re.fullmatch(r"s_waitcnt vmcnt\(0\)", s)]
+        assert late == [], (k, len(late))
     assert found
