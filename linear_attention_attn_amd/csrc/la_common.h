@@ -198,21 +198,6 @@ __device__ __forceinline__ void dma_lds16(__amdgpu_buffer_rsrc_t r, char *lds, u
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
 }
 
-// The same buffer-to-LDS load from inline asm, outside the compiler's view:
-// it inserts no wait of its own for it, so the caller's explicit waits
-// (before the barriers that publish each tile) are the only ones.  The LDS
-// address (wave-uniform) goes to M0 in the same statement; the instruction
-// has no result registers.
-__device__ __forceinline__ void dma_lds16_asm(__amdgpu_buffer_rsrc_t r, const char *lds, uint32_t voff,
-                                              uint32_t soff) {
-    const uint32_t a = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)lds);
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-                 :
-                 : "v"(voff), "s"(r), "s"(soff), "s"(a)
-                 : "memory", "m0");
-}
-
 // 16-byte buffer store from inline asm, so that the compiler's vmcnt
 // bookkeeping holds loads only (it treats a counter with loads and stores
 // pending as unordered and then waits for everything).  The s_nop keeps the

@@ -96,13 +96,15 @@ def test_integer_exact(dev, dt, d, B, n, C, S):
     assert np.array_equal(o.astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("B", [128, 256])
+@pytest.mark.parametrize("B", [64, 128, 256])
 @pytest.mark.parametrize("C", [0, 512])
-def test_partial_last_block_exact(dev, d, B, C):
+def test_partial_last_block_exact(dev, dt, d, B, C):
     """Sequences ending on both sides of every 16-row slab and 64-token tile
     edge inside their last block, where the kernel skips the slabs and keys
-    past the end and stops after the last tile with tokens: integer-exact
+    past the end and stops after the last tile with tokens (fp32 with d = 64:
+    the ring kernel, which stops the same way): integer-exact
     inputs, so o and the final states must equal the oracle bit for bit;
     dense (one length per call) and packed (all lengths in one call), with
     one chunk per sequence (C = 0) and with chunks of 512 tokens."""
@@ -111,18 +113,18 @@ def test_partial_last_block_exact(dev, d, B, C):
     ends = [1, 15, 16, 17, 63, 64, 65, 127, 129, 191, 192, 193, B - 1]
     lengths = [e for e in ends if e < B] + [B + 47, 2 * B + 80, 3 * B - 1]
     rng = np.random.default_rng(d + B + C)
-    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch_dtype(dt))
     H = 2
     with chunk_tokens(C):
         for n in lengths:
-            note(f"partial last block dense d={d} B={B} C={C} n={n}")
+            note(f"partial last block dense dt={dt} d={d} B={B} C={C} n={n}")
             qh, kh, vh = _onehot_inputs(rng, (1, H, n, d))
             Sf = torch.full((1, H, d, d), float("nan"), device=dev)
             o = host(la.fwd(t(qh), t(kh), t(vh), block_size=B, s_final=Sf))
             ref, sref = oracle.causal_linear_attention_state(qh, kh, vh)
             assert np.array_equal(o.astype(np.float64), ref), n
             assert np.array_equal(host(Sf).astype(np.float64), sref), n
-        note(f"partial last block packed d={d} B={B} C={C}")
+        note(f"partial last block packed dt={dt} d={d} B={B} C={C}")
         cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
         T = int(cu[-1])
         qh, kh, vh = _onehot_inputs(rng, (H, T, d))
