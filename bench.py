@@ -91,6 +91,21 @@ def profiled_traffic(workload_name):
     return float(fields["traffic_bytes_per_launch"])
 
 
+STAGES = ["tables", "summary", "scan", "fused"]
+
+
+def stage_times(hip, evs, used, steps):
+    """Mean ms per stage from the library's stage events (stage j runs from
+    event j to event j + 1); a stage whose opening event was not recorded
+    launched nothing and counts 0.  events_total spans the recorded ones."""
+    out = {}
+    for j, n in enumerate(STAGES):
+        out[n] = (sum(hip.ms(e[j], e[j + 1]) for e in evs) / steps) if used[j] else 0.0
+    first = used.index(True)
+    out["events_total"] = sum(hip.ms(e[first], e[4]) for e in evs) / steps
+    return out
+
+
 def prefill_flops_per_head_token(d, B):
     """Algorithmic work: 2d^2 (Q S) + 2d^2 (K^T V) + 2d(B+1) (causal half of the
     intra-block Q K^T and P V, diagonal included)."""
@@ -120,13 +135,19 @@ def bench_prefill(w, steps, warmup, dev, traced=True):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    chunk = la.lightning_attn_fwd_chunk_tokens(w.batch, w.heads, w.seq_len, w.head_dim,
+                                               w.block_size, 0, code)
+    # dense input builds no tables; one chunk per sequence runs no summaries
+    # or scan: only the events around stages that launch work are recorded
+    used = [False, True, True, True, True] if chunk < w.seq_len else [False, False, False, True, True]
     hip = HipEvents()
     evs = [hip.create(la.LA_FWD_NUM_EVENTS) for _ in range(steps)] if traced else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         if traced:
-            st = la.lightning_attn_fwd_traced(*args, evs[i], la.LA_FWD_NUM_EVENTS)
+            rec = [e if u else None for e, u in zip(evs[i], used)]
+            st = la.lightning_attn_fwd_traced(*args, rec, la.LA_FWD_NUM_EVENTS)
             if st != la.LA_OK:
                 raise la.LightningAttnError(st, "lightning_attn_fwd_traced")
         else:
@@ -135,17 +156,9 @@ def bench_prefill(w, steps, warmup, dev, traced=True):
     t1 = time.perf_counter()
     stage = None
     if traced:
-        names = ["tables", "summary", "scan", "fused"]
-        acc = [0.0] * 4
-        for e in evs:
-            for j in range(4):
-                acc[j] += hip.ms(e[j], e[j + 1])
-        stage = {n: acc[j] / steps for j, n in enumerate(names)}
-        stage["events_total"] = sum(hip.ms(e[0], e[4]) for e in evs) / steps
+        stage = stage_times(hip, evs, used, steps)
         for e in evs:
             hip.destroy(e)
-    chunk = la.lightning_attn_fwd_chunk_tokens(w.batch, w.heads, w.seq_len, w.head_dim,
-                                               w.block_size, 0, code)
     del q, k, v, o, ws
     torch.cuda.empty_cache()
     return (t1 - t0) * 1000.0 / steps, stage, chunk, nbytes
@@ -184,8 +197,7 @@ def bench_prefill_varlen(w, steps, warmup, dev):
             raise la.LightningAttnError(st, "lightning_attn_fwd_traced")
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    names = ["tables", "summary", "scan", "fused"]
-    stage = {n: sum(hip.ms(e[j], e[j + 1]) for e in evs) / steps for j, n in enumerate(names)}
+    stage = stage_times(hip, evs, [True] * la.LA_FWD_NUM_EVENTS, steps)
     for e in evs:
         hip.destroy(e)
     chunk = la.lightning_attn_fwd_chunk_tokens(w.batch, w.heads, T, w.head_dim, w.block_size, 1, code)

@@ -140,8 +140,12 @@ int lightning_attn_fwd_state(const void *q, const void *k, const void *v, void *
  *   events[2] after the per-chunk K^T V summaries,
  *   events[3] after the exclusive scan of chunk states,
  *   events[4] after the fused intra-block + Q S output kernel.
- * nevents must be LA_FWD_NUM_EVENTS; a NULL events pointer or a NULL entry is
- * LA_EINVAL.  The events are only recorded, never synchronised or destroyed.
+ * nevents must be LA_FWD_NUM_EVENTS and events non-NULL (else LA_EINVAL); a
+ * NULL entry is not recorded, so a caller can bracket only the stages it
+ * times (each recorded event takes a little time on the stream).  Stages with
+ * nothing to do launch nothing: dense input builds no tables, and a plan of
+ * one chunk per sequence runs no summaries or scan.  The events are only
+ * recorded, never synchronised or destroyed.
  */
 #define LA_FWD_NUM_EVENTS 5
 int lightning_attn_fwd_traced(const void *q, const void *k, const void *v, void *o,

@@ -324,8 +324,6 @@ int lightning_attn_fwd_traced(const void *q, const void *k, const void *v, void 
                               size_t workspace_bytes, void *stream, void *const *events,
                               int nevents) {
     if (!events || nevents != LA_FWD_NUM_EVENTS) return LA_EINVAL;
-    for (int i = 0; i < nevents; ++i)
-        if (!events[i]) return LA_EINVAL;
     return fwd_common(q, k, v, o, batch, heads, seq_len, head_dim, block_size, cu_seqlens, dtype,
                       nullptr, nullptr, workspace, workspace_bytes, stream, events);
 }

@@ -9,7 +9,9 @@
 //
 // Kernels (all on the caller's stream, no host synchronisation):
 //   1. k_prep       chunk, sub-chunk and scan-tile offset tables from
-//                   cu_seqlens (1 WG)
+//                   cu_seqlens (1 WG; packed input only: for dense input
+//                   every sequence has the same counts and the offsets are
+//                   products)
 //   2. k_summary    U_c = K_c^T V_c for every sub-chunk c of C_s tokens that
 //                   precedes a sequence's last chunk (MFMA)
 //   3. k_scan_*     fp32 exclusive prefix over sub-chunk states, segmented at
@@ -57,6 +59,9 @@ struct KParams {
     int64_t chunk;          // tokens per chunk (a multiple of sub)
     int64_t sub;            // tokens per sub-chunk
     int64_t nchunk_ub, nsub_ub, ntile_ub;
+    // dense input: chunks, sub-chunk entries and scan tiles per sequence (the
+    // same for every sequence, so the offset tables are products)
+    int64_t cps, nsps, tps;
     int nseq, heads, group;
     // state handoff: initial states [nseq][heads][D][D] (or nullptr = zero)
     // and final states of the same layout (or nullptr = not wanted).
@@ -109,6 +114,26 @@ __device__ __forceinline__ int find_seg(const int32_t *off, int n, int64_t x) {
     return lo;
 }
 
+// Chunks, sub-chunk entries and scan tiles before sequence s.  Packed input:
+// the tables k_prep builds from cu_seqlens; dense input: every sequence has
+// the same counts, so no tables are built and these are products.
+__device__ __forceinline__ int64_t chunk_off(const KParams &p, int s) {
+    return p.cu ? (int64_t)p.chunk_off[s] : (int64_t)s * p.cps;
+}
+__device__ __forceinline__ int64_t sub_off(const KParams &p, int s) {
+    return p.cu ? (int64_t)p.sub_off[s] : (int64_t)s * p.nsps;
+}
+__device__ __forceinline__ int64_t tile_off(const KParams &p, int s) {
+    return p.cu ? (int64_t)p.tile_off[s] : (int64_t)s * p.tps;
+}
+// The sequence of sub-chunk entry x, resp. scan tile x (x below the total).
+__device__ __forceinline__ int seq_of_sub(const KParams &p, int64_t x) {
+    return p.cu ? find_seg(p.sub_off, p.nseq, x) : (int)(x / p.nsps);
+}
+__device__ __forceinline__ int seq_of_tile(const KParams &p, int64_t x) {
+    return p.cu ? find_seg(p.tile_off, p.nseq, x) : (int)(x / p.tps);
+}
+
 // The (head, chunk, sequence) of a chunk workgroup, or false when the
 // workgroup has no chunk.  Workgroups are taken in dispatch order with the
 // head varying fastest, so all heads of one chunk slot start together; with
@@ -119,14 +144,14 @@ __device__ __forceinline__ bool chunk_of_block(const KParams &p, int &h, int64_t
     const int64_t lin = (int64_t)blockIdx.x + (int64_t)gridDim.x * blockIdx.y;
     h = (int)(lin % p.heads);
     const int64_t slot = lin / p.heads;
-    if (slot >= p.chunk_off[p.nseq]) return false;
+    if (slot >= chunk_off(p, p.nseq)) return false;
     if (p.slot_tab != nullptr) {        // one load instead of a search over the ranking
         const int2 e = reinterpret_cast<const int2 *>(p.slot_tab)[slot];
         s = e.x;
         gch = e.y;
     } else {                            // dense: every sequence has the same chunk count
         gch = slot;
-        s = (int)(gch / ((p.seq_len + p.chunk - 1) / p.chunk));
+        s = (int)(gch / p.cps);
     }
     return true;
 }
@@ -149,20 +174,20 @@ __device__ __forceinline__ int64_t state_entry(const KParams &p, int s) {
 // copies it first, since the last chunk's workgroup writes the final state).
 template <int D>
 __device__ __forceinline__ const float *chunk_start_state(const KParams &p, int s, int h, int64_t cl) {
-    if (p.init_mode == 2 || p.chunk_off[s + 1] - p.chunk_off[s] == 1) {
+    if (p.init_mode == 2 || chunk_off(p, s + 1) - chunk_off(p, s) == 1) {
         const int64_t e = p.init_mode == 0 ? -1 : state_entry(p, s);
         return e < 0 ? nullptr : p.s_init + (e * p.heads + h) * (D * D);
     }
     if (p.init_mode == 0 && cl == 0) return nullptr;
-    const int64_t gsub = p.sub_off[s] + cl * (p.chunk / p.sub);
+    const int64_t gsub = sub_off(p, s) + cl * (p.chunk / p.sub);
     return p.states + ((int64_t)h * p.nsub_ub + gsub) * (D * D);
 }
 
 // Sub-chunk gsub of sequence s, or -1 when its summary is not needed (it lies
 // in the sequence's last chunk): its first token otherwise.
 __device__ __forceinline__ int64_t sub_first_token(const KParams &p, int s, int64_t gsub) {
-    const int64_t t0 = (gsub - p.sub_off[s]) * p.sub;
-    const int64_t nc = p.chunk_off[s + 1] - p.chunk_off[s];
+    const int64_t t0 = (gsub - sub_off(p, s)) * p.sub;
+    const int64_t nc = chunk_off(p, s + 1) - chunk_off(p, s);
     return t0 >= (nc - 1) * p.chunk ? -1 : t0;
 }
 
@@ -170,7 +195,7 @@ __device__ __forceinline__ int64_t sub_first_token(const KParams &p, int s, int6
 // sequence's last: the workgroup of that chunk writes it; else nullptr.
 template <int D>
 __device__ __forceinline__ float *final_state_dst(const KParams &p, int s, int h, int64_t gch) {
-    if (p.s_final == nullptr || gch + 1 != p.chunk_off[s + 1]) return nullptr;
+    if (p.s_final == nullptr || gch + 1 != chunk_off(p, s + 1)) return nullptr;
     const int64_t e = state_entry(p, s);
     return e < 0 ? nullptr : p.s_final + (e * p.heads + h) * (D * D);
 }
@@ -511,8 +536,8 @@ __global__ __launch_bounds__(512, 2) void k_summary(KParams p) {
     __shared__ __attribute__((aligned(16))) char lds[2][2 * C::KT_BYTES];
     const int h = blockIdx.y;
     const int64_t gch = blockIdx.x;
-    if (gch >= p.sub_off[p.nseq]) return;
-    const int s = find_seg(p.sub_off, p.nseq, gch);
+    if (gch >= sub_off(p, p.nseq)) return;
+    const int s = seq_of_sub(p, gch);
     const int64_t t0 = sub_first_token(p, s, gch);
     if (t0 < 0) return;                              // in the sequence's last chunk: not needed
     const Unit u = unit_of<D>(p, s, h);
@@ -571,10 +596,10 @@ template <int D>
 __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(KParams p) {
     const int h = blockIdx.z;
     const int64_t tile = blockIdx.x;
-    if (tile >= p.tile_off[p.nseq]) return;
-    const int s = find_seg(p.tile_off, p.nseq, tile);
-    const int64_t c0 = p.sub_off[s] + (tile - p.tile_off[s]) * p.group;
-    const int64_t c1 = min((int64_t)p.sub_off[s + 1], c0 + p.group);
+    if (tile >= tile_off(p, p.nseq)) return;
+    const int s = seq_of_tile(p, tile);
+    const int64_t c0 = sub_off(p, s) + (tile - tile_off(p, s)) * p.group;
+    const int64_t c1 = min(sub_off(p, s + 1), c0 + p.group);
     const int e = blockIdx.y * kScanThreads + threadIdx.x;
     const float *src = p.states + (int64_t)h * p.nsub_ub * (D * D) + e;
     float acc = 0.f;
@@ -588,13 +613,13 @@ template <int D>
 __global__ __launch_bounds__(kScanThreads) void k_scan_tiles(KParams p) {
     const int h = blockIdx.z;
     const int64_t tile = blockIdx.x;
-    if (tile >= p.tile_off[p.nseq]) return;
-    const int s = find_seg(p.tile_off, p.nseq, tile);
-    if (tile != p.tile_off[s]) return;
+    if (tile >= tile_off(p, p.nseq)) return;
+    const int s = seq_of_tile(p, tile);
+    if (tile != tile_off(p, s)) return;
     const int e = blockIdx.y * kScanThreads + threadIdx.x;
     float *ts = p.tilesum + (int64_t)h * p.ntile_ub * (D * D) + e;
     float run = 0.f;
-    for (int64_t t = p.tile_off[s]; t < p.tile_off[s + 1]; ++t) {
+    for (int64_t t = tile_off(p, s); t < tile_off(p, s + 1); ++t) {
         const float x = ts[t * (D * D)];
         ts[t * (D * D)] = run;
         run += x;
@@ -605,10 +630,10 @@ template <int D>
 __global__ __launch_bounds__(kScanThreads) void k_scan_apply(KParams p, int use_tiles) {
     const int h = blockIdx.z;
     const int64_t tile = blockIdx.x;
-    if (tile >= p.tile_off[p.nseq]) return;
-    const int s = find_seg(p.tile_off, p.nseq, tile);
-    const int64_t c0 = p.sub_off[s] + (tile - p.tile_off[s]) * p.group;
-    const int64_t c1 = min((int64_t)p.sub_off[s + 1], c0 + p.group);
+    if (tile >= tile_off(p, p.nseq)) return;
+    const int s = seq_of_tile(p, tile);
+    const int64_t c0 = sub_off(p, s) + (tile - tile_off(p, s)) * p.group;
+    const int64_t c1 = min(sub_off(p, s + 1), c0 + p.group);
     const int e = blockIdx.y * kScanThreads + threadIdx.x;
     float *st = p.states + (int64_t)h * p.nsub_ub * (D * D) + e;
     float run = use_tiles ? p.tilesum[((int64_t)h * p.ntile_ub + tile) * (D * D) + e] : 0.f;
@@ -617,7 +642,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_apply(KParams p, int use_
         if (se >= 0) run += p.s_init[(se * p.heads + h) * (D * D) + e];
     }
     const int64_t per = p.chunk / p.sub;
-    int64_t j = (c0 - p.sub_off[s]) % per;            // sub-chunk index within its chunk
+    int64_t j = (c0 - sub_off(p, s)) % per;           // sub-chunk index within its chunk
     for (int64_t c = c0; c < c1; ++c) {
         const float x = st[c * (D * D)];
         if (j == 0) st[c * (D * D)] = run;
@@ -651,7 +676,7 @@ __global__ __launch_bounds__(512, 1) void k_fused(KParams p) {
     int64_t gch;
     if (!chunk_of_block(p, h, gch, s)) return;
     const Unit u = unit_of<D>(p, s, h);
-    const int64_t cl = gch - p.chunk_off[s];
+    const int64_t cl = gch - chunk_off(p, s);
     const int64_t t0 = cl * p.chunk;
     const int64_t t1 = min(u.len, t0 + p.chunk);
     const T *qb = reinterpret_cast<const T *>(p.q) + u.base;
@@ -999,7 +1024,7 @@ __global__ __launch_bounds__(512, 1) void k_fused_ring(KParams p) {
     int64_t gch;
     if (!chunk_of_block(p, h, gch, s)) return;
     const Unit u = unit_of<D>(p, s, h);
-    const int64_t cl = gch - p.chunk_off[s];
+    const int64_t cl = gch - chunk_off(p, s);
     const int64_t t0 = cl * p.chunk;
     const int n = (int)min(u.len - t0, p.chunk);     // tokens of this chunk
     const int64_t t1 = t0 + n;
@@ -1302,8 +1327,8 @@ __global__ __launch_bounds__(NW * 64, 1024 / (NW * 64)) void k_summary_reg(KPara
     Ring<2, SBY>::get(stages);
     const int h = blockIdx.y;
     const int gch = blockIdx.x;
-    if (gch >= p.sub_off[p.nseq]) return;
-    const int s = find_seg(p.sub_off, p.nseq, gch);
+    if (gch >= sub_off(p, p.nseq)) return;
+    const int s = seq_of_sub(p, gch);
     const int64_t t0 = sub_first_token(p, s, gch);
     if (t0 < 0) return;                              // in the sequence's last chunk: not needed
     const Unit u = unit_of<D>(p, s, h);
@@ -1504,7 +1529,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
     int64_t gch;
     if (!chunk_of_block(p, h, gch, s)) return;
     const Unit u = unit_of<D>(p, s, h);
-    const int cl = gch - p.chunk_off[s];
+    const int cl = (int)(gch - chunk_off(p, s));
     const int64_t t0 = (int64_t)cl * p.chunk;
     const int n = (int)min(u.len - t0, p.chunk);     // tokens of this chunk
     const int64_t cb = (u.base + t0 * D) * 2;        // byte offset of its first row
@@ -1930,14 +1955,19 @@ constexpr int fused_waves(int D, int BLK) { return BLK == 64 ? 8 : 16; }
 template <typename T, int D, int BLK, bool ROPE>
 static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream_t st, void *const *ev) {
     auto mark = [&](int i) {
-        if (ev) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), st);
+        if (ev && ev[i]) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(ev[i]), st);
     };
     const dim3 gchunks((unsigned)plan.nchunk_ub, (unsigned)kp.heads);
     const dim3 gsubs((unsigned)plan.nsub_ub, (unsigned)kp.heads);
     mark(0);
-    hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, st, kp);
-    if (kp.s_final && !kp.slots)
-        hipLaunchKernelGGL(k_state_empty<D>, dim3(kp.nseq, kp.heads), dim3(256), 0, st, kp);
+    // packed input: the offset tables from cu_seqlens (dense input needs none),
+    // and the final states of sequences with no tokens (every dense sequence
+    // has tokens here: a call with none never reaches the kernels)
+    if (kp.cu) {
+        hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, st, kp);
+        if (kp.s_final && !kp.slots)
+            hipLaunchKernelGGL(k_state_empty<D>, dim3(kp.nseq, kp.heads), dim3(256), 0, st, kp);
+    }
     mark(1);
     // Every chunk but the first of its sequence needs the exclusive prefix of
     // the chunk summaries before it; with one chunk per sequence there is none.
@@ -2047,6 +2077,14 @@ int launch_fwd(const FwdArgs &a, void *stream, void *const *events) {
     kp.nseq = a.nseq;
     kp.heads = a.heads;
     kp.group = a.plan.scan_group;
+    if (!a.cu_seqlens) {                             // dense: the same counts for every sequence
+        const int64_t C = a.plan.chunk, Cs = a.plan.sub, G = a.plan.scan_group;
+        kp.cps = (a.seq_len + C - 1) / C;
+        kp.nsps = kp.cps >= 2 ? (kp.cps - 1) * (C / Cs) + 1 : 0;
+        kp.tps = (kp.nsps + G - 1) / G;
+    } else {
+        kp.cps = kp.nsps = kp.tps = 0;
+    }
     kp.s_init = a.s_init;
     kp.s_final = a.s_final;
     kp.slots = a.slots;

@@ -226,6 +226,16 @@ def test_noalloc_refuses_on_the_host(la):
     assert la.lightning_attn_strerror(la.LA_ESCRATCH) != "unknown status"
 
 
+def test_traced_rejects_missing_event_array(la):
+    fake = 1 << 20
+    need = la.lightning_attn_fwd_workspace_size(1, 1, 10, 64, 64, 0, 0)
+    lib = la.load_library()
+    assert lib.lightning_attn_fwd_traced(fake, fake, fake, fake, 1, 1, 10, 64, 64, None, 0, fake, need, None,
+                                         None, la.LA_FWD_NUM_EVENTS) == 1
+    assert la.lightning_attn_fwd_traced(fake, fake, fake, fake, 1, 1, 10, 64, 64, None, 0, fake, need, None,
+                                        [None] * 4, 4) == 1
+
+
 def test_product_never_imports_oracle():
     """The HIP path must not route through the CPU oracle."""
     pkg = os.path.join(ROOT, "linear_attention_attn_amd")

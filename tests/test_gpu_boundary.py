@@ -71,6 +71,11 @@ def test_traced_equals_plain(dev, shape, packed):
     evs = hip.create(la.LA_FWD_NUM_EVENTS)
     assert la.lightning_attn_fwd_traced(q, k, v, o2, batch, heads, T, d, 256, cu, code, ws, nbytes, stream,
                                         evs, la.LA_FWD_NUM_EVENTS) == 0
+    # with only the fused kernel bracketed (NULL entries are not recorded)
+    o4 = torch.full_like(q, float("nan"))
+    part = hip.create(2)
+    assert la.lightning_attn_fwd_traced(q, k, v, o4, batch, heads, T, d, 256, cu, code, ws, nbytes, stream,
+                                        [None, None, None, part[0], part[1]], la.LA_FWD_NUM_EVENTS) == 0
     wsp = la.lightning_attn_fwd_workspace_size_planned(batch, heads, T, d, 256, varlen, code, 0, 0)
     assert wsp == nbytes
     assert la.lightning_attn_fwd_planned(q, k, v, o3, batch, heads, T, d, 256, cu, code, None, None, None, 0,
@@ -78,11 +83,14 @@ def test_traced_equals_plain(dev, shape, packed):
     torch.cuda.synchronize()
     stages = [hip.ms(evs[i], evs[i + 1]) for i in range(la.LA_FWD_NUM_EVENTS - 1)]
     total = hip.ms(evs[0], evs[-1])
+    assert hip.ms(part[0], part[1]) > 0
     hip.destroy(evs)
+    hip.destroy(part)
     chunk = la.lightning_attn_fwd_chunk_tokens(batch, heads, T, d, 256, varlen, code)
     print(f"chunk {chunk} stages {['%.3f' % x for x in stages]} total {total:.3f} ms")
     assert all(x >= 0 for x in stages) and abs(sum(stages) - total) < 1e-3 + 1e-3 * total
     a = o1.view(torch.int16).cpu().numpy()
     assert np.array_equal(a, o2.view(torch.int16).cpu().numpy())
     assert np.array_equal(a, o3.view(torch.int16).cpu().numpy())
+    assert np.array_equal(a, o4.view(torch.int16).cpu().numpy())
     assert not torch.isnan(o1).any()
