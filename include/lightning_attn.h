@@ -41,7 +41,10 @@ extern "C" {
 /* Status codes. */
 #define LA_OK           0  /* success (launches queued on the stream)               */
 #define LA_EINVAL       1  /* NULL pointer with work to do, or a negative/zero size */
-#define LA_EUNSUPPORTED 2  /* head_dim not 64/128, block_size not 64/128/256, or dtype unknown */
+#define LA_EUNSUPPORTED 2  /* head_dim not 64/128, block_size not 64/128/256, dtype unknown, or a
+                              shape past the limits of one launch (more than 2^32 - 1 threads
+                              along the grid: over ~4.19M chunks in a prefill, or batch x heads
+                              of 2^24 or more in a decode step) */
 #define LA_EWORKSPACE   3  /* workspace NULL or smaller than the size query returned */
 #define LA_EHIP         4  /* a HIP launch failed; see hipGetLastError semantics     */
 #define LA_ESCRATCH     5  /* lightning_attn_fwd_noalloc: the call needs more scratch than

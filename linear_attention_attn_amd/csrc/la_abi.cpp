@@ -34,6 +34,12 @@ static bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 // int32 tables (cu_seqlens, slots, positions, offsets).
 static bool aligned4(const void *p) { return ((uintptr_t)p & 3) == 0; }
 
+// The decode step runs one 256-thread workgroup per (row, head): at most
+// 2^32 - 1 work-items in one launch.
+static bool decode_grid_ok(int batch, int heads) {
+    return (int64_t)batch * heads * 256 <= ((int64_t)1 << 32) - 1;
+}
+
 static int64_t env_i64(const char *name, int64_t dflt) {
     const char *s = getenv(name);
     if (!s || !*s) return dflt;
@@ -141,6 +147,12 @@ int make_fwd_plan(int batch, int heads, int64_t seq_len, int head_dim, int block
         p.scan_tiles = cdiv(seq_len, Cs) > G;
         p.single_chunk = seq_len <= C;   // no sequence is longer than the whole input
     }
+    // One launch covers at most 2^32 - 1 work-items along x: the fused
+    // kernels run up to 1024 threads per chunk, the summaries 512 per
+    // sub-chunk, the scan and empty-state kernels 256 per tile or sequence.
+    const int64_t kMaxX = ((int64_t)1 << 32) - 1;
+    if (p.nchunk_ub * 1024 > kMaxX || (int64_t)batch * 256 > kMaxX) return LA_EUNSUPPORTED;
+    if (!p.single_chunk && (p.nsub_ub * 512 > kMaxX || p.ntile_ub * 256 > kMaxX)) return LA_EUNSUPPORTED;
     const size_t dd = (size_t)head_dim * head_dim * sizeof(float);
     size_t off = 0;
     p.off_chunk_off = off;
@@ -333,7 +345,7 @@ int lightning_attn_decode(const void *q, const void *k, const void *v, float *st
     if (!(dtype == LA_DTYPE_BF16 || dtype == LA_DTYPE_F32)) return LA_EUNSUPPORTED;
     if (head_dim != 64 && head_dim != 128) return LA_EUNSUPPORTED;
     if (batch < 1 || heads < 1) return LA_EINVAL;
-    if ((int64_t)batch * heads > (int64_t)INT32_MAX) return LA_EUNSUPPORTED;
+    if (!la::decode_grid_ok(batch, heads)) return LA_EUNSUPPORTED;
     if (!q || !k || !v || !state || !o) return LA_EINVAL;
     if (!la::aligned16(state)) return LA_EINVAL;
     return la::launch_decode(q, k, v, state, o, batch, heads, head_dim, dtype, stream) == 0 ? LA_OK : LA_EHIP;
@@ -345,7 +357,7 @@ int lightning_attn_decode_indexed(const void *q, const void *k, const void *v, f
     if (!(dtype == LA_DTYPE_BF16 || dtype == LA_DTYPE_F32)) return LA_EUNSUPPORTED;
     if (head_dim != 64 && head_dim != 128) return LA_EUNSUPPORTED;
     if (batch < 1 || heads < 1 || nslots < 0) return LA_EINVAL;
-    if ((int64_t)batch * heads > (int64_t)INT32_MAX || (int64_t)nslots * heads > (int64_t)INT32_MAX)
+    if (!la::decode_grid_ok(batch, heads) || (int64_t)nslots * heads > (int64_t)INT32_MAX)
         return LA_EUNSUPPORTED;
     if (!q || !k || !v || !slots || !o || (nslots > 0 && !state_pool)) return LA_EINVAL;
     if (!la::aligned16(state_pool) || !la::aligned4(slots)) return LA_EINVAL;
@@ -363,7 +375,7 @@ int lightning_attn_decode_rope(const void *q, const void *k, const void *v, floa
     const int rs = check_rope(rope_dims, rope_base, head_dim);
     if (rs != LA_OK) return rs;
     if (batch < 1 || heads < 1) return LA_EINVAL;
-    if ((int64_t)batch * heads > (int64_t)INT32_MAX) return LA_EUNSUPPORTED;
+    if (!la::decode_grid_ok(batch, heads)) return LA_EUNSUPPORTED;
     if (!q || !k || !v || !o || !positions) return LA_EINVAL;
     if (!la::aligned16(state) || !la::aligned4(positions) || !la::aligned4(slots)) return LA_EINVAL;
     if (slots) {

@@ -121,6 +121,26 @@ def test_decode_rejects(la):
     assert la.lightning_attn_decode(fake, fake, fake, None, fake, 1, 1, 64, 0, None) == 1
 
 
+def test_launch_grid_limits(la):
+    """Shapes whose launches would exceed 2^32 - 1 work-items along the grid's
+    x axis are refused on the host as unsupported, not left to fail at launch."""
+    fake = 1 << 20
+    # decode: one 256-thread workgroup per (row, head)
+    assert la.lightning_attn_decode(fake, fake, fake, fake, fake, 1 << 24, 1, 64, 0, None) == 2
+    assert la.lightning_attn_decode(fake, fake, fake, fake, fake, 1 << 23, 2, 64, 0, None) == 2
+    assert la.lightning_attn_decode_indexed(fake, fake, fake, fake, 1, fake, fake, 1 << 24, 1, 64, 0,
+                                            None) == 2
+    assert la.lightning_attn_decode_rope(fake, fake, fake, fake, 0, None, fake, 1 << 24, 1, 64, 0, 32, 1e4,
+                                         fake, None) == 2
+    # prefill: one fused workgroup (up to 1024 threads) per chunk; 2^22
+    # one-chunk sequences is the first count past the limit
+    assert la.lightning_attn_fwd_workspace_size((1 << 22) - 1, 1, 64, 64, 64, 0, 0) > 0
+    assert la.lightning_attn_fwd_workspace_size(1 << 22, 1, 64, 64, 64, 0, 0) == 0
+    need = la.lightning_attn_fwd_workspace_size(1, 1, 10, 64, 64, 0, 0)
+    assert la.lightning_attn_fwd(fake, fake, fake, fake, 1 << 22, 1, 64, 64, 64, None, 0, fake, need,
+                                 None) == 2
+
+
 def test_rope_rejects(la):
     """Rotary arguments are checked on the host before any launch."""
     fake = 1 << 20
