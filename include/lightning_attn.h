@@ -95,8 +95,9 @@ int64_t lightning_attn_fwd_chunk_tokens(int batch, int heads, int64_t seq_len, i
  * workspace: device memory of at least lightning_attn_fwd_workspace_size(...)
  * bytes (same arguments, varlen = cu_seqlens != NULL), 256-byte aligned.
  *
- * q, k, v, o and the workspace must be 16-byte aligned and cu_seqlens 4-byte
- * aligned (else LA_EINVAL; the kernels move 16-byte vectors).
+ * q, k, v and o must be 16-byte aligned (the kernels move 16-byte vectors),
+ * the workspace 256-byte aligned and cu_seqlens 4-byte aligned (else
+ * LA_EINVAL).
  * All argument checks happen on the host before any launch (the contents of
  * cu_seqlens, which live on the device, are checked by the first kernel as
  * described above); a rejected call writes nothing.  seq_len == 0 returns LA_OK without touching any pointer.
