@@ -1016,7 +1016,15 @@ __global__ __launch_bounds__(512, 1) void k_fused_ring(KParams p) {
     constexpr int NI = TB / 1024;                    // 1 KiB loads per tensor tile
     constexpr int IPW = 2 * NI / C::NW;              // loads per wave per tile
     static_assert(C::NW == 8 && IPW == 2 && C::KR_ROW == RB && TPB >= 2, "tile split");
+    // Blocks of 64 (one row slab per wave, two waves per slab): the two
+    // waves of a slab split each tile's keys instead of the output columns,
+    // so neither recomputes the other's scores.  Each then holds a partial O
+    // for all four column tiles; at the block's end it hands the partner's
+    // two column tiles over through LDS (exchange buffer: 2 KiB per wave).
+    constexpr bool KS = C::NSW == 1 && C::CSPLIT == 2;
+    constexpr int NCO = KS ? 2 * C::NCT : C::NCT;   // O column tiles held per wave
     __shared__ __attribute__((aligned(16))) char st[C::ST_BYTES];
+    __shared__ __attribute__((aligned(16))) char xbuf[KS ? C::NW * 2048 : 16];
     char *stages[NST];
     Ring<NST, SBY>::get(stages);
 
@@ -1038,6 +1046,7 @@ __global__ __launch_bounds__(512, 1) void k_fused_ring(KParams p) {
     const int w = wave_id(), l = lane_id(), c = l & 15, g = l >> 4;
     const int a0 = C::SA * (w % C::AW), b0 = C::SB * (w / C::AW);
     const int ct0 = C::CSPLIT == 1 ? 0 : (w >> 2) * C::NCT;
+    const int hk = w >> 2;                           // key half of a tile (key split)
     const int nblk = (n + BLK - 1) / BLK;
     const int ntile = (n + TJ - 1) / TJ;             // tiles holding tokens
     const int nsb = (ntile + NST - 1) / NST;
@@ -1124,7 +1133,9 @@ __global__ __launch_bounds__(512, 1) void k_fused_ring(KParams p) {
     wait_vm_lgkm0<IPW>();
     wg_barrier();
 
-    f32x4_t O[C::NSW][C::NCT];
+    // O[si][m]: column tile ct0 + m (with the key split, m = 2, 3 are the
+    // partner's column tiles ct0 + 2, ct0 + 3 modulo 4)
+    f32x4_t O[C::NSW][NCO];
     using std::integral_constant;
     auto tile = [&](auto J_c, int sb) {
         constexpr int J = decltype(J_c)::value;     // ring stage of the tile
@@ -1147,7 +1158,7 @@ __global__ __launch_bounds__(512, 1) void k_fused_ring(KParams p) {
 #pragma unroll
             for (int si = 0; si < C::NSW; ++si)
 #pragma unroll
-                for (int ct = 0; ct < C::NCT; ++ct) O[si][ct] = zero4();
+                for (int ct = 0; ct < NCO; ++ct) O[si][ct] = zero4();
 #pragma unroll
             for (int ct = 0; ct < C::NCT; ++ct)
 #pragma unroll
@@ -1159,7 +1170,33 @@ __global__ __launch_bounds__(512, 1) void k_fused_ring(KParams p) {
         }
         // ---- intra-block left product for this K/V tile (keys jt*TJ .. of the block)
         const int left = (int)(t1 - tb);             // tokens of the chunk from this block on
-        {
+        if constexpr (KS) {
+            // this wave's 16 keys jh .. jh + 15 of the tile against its slab's
+            // rows, then P V over all four column tiles
+            const int i0 = 16 * slab_of<BLK>(w, 0);
+            const int kmax = i0 < left ? min(i0 + 15, left - 1) : -1;   // last key the slab sees
+            const int jh = jt * TJ + 16 * hk;
+            if (jh <= kmax) {
+                f32x4_t P = zero4();
+#pragma unroll
+                for (int kc = 0; kc < C::KC; ++kc)
+                    mma(P, lds_read8<T, C::KR_ROW>(kr, 16 * hk + c, kc * 32 + 8 * g), Q[0][kc]);
+                const int i = i0 + c;                  // block-local query row
+                if (jh + 15 > i0) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (jh + 4 * g + r > i) P[r] = 0.f;
+                }
+#pragma unroll
+                for (int m = 0; m < NCO; ++m) {
+                    // keys 16 hk + 4g .. +3 of the transposed V rows of column tile ct0 + m
+                    const f32x4_t a = *reinterpret_cast<const f32x4_t *>(
+                        vt + LdsRows<C::KT_ROW>::off(((ct0 + m) & 3) * 16 + c, (16 * hk + 4 * g) * 4));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) O[0][m] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], P[r], O[0][m], 0, 0, 0);
+                }
+            }
+        } else {
             const int jb = jt * TJ;
             f32x4_t P[C::NSW][2];
             bool need[C::NSW], need1[C::NSW];
@@ -1219,6 +1256,18 @@ __global__ __launch_bounds__(512, 1) void k_fused_ring(KParams p) {
         // ---- state for the next block
         if (more || fdst) state_update<T, D, BLK, C::SA, C::SB>(S, kt, vt, a0, b0);
         if (block_end) {
+            if constexpr (KS) {
+                // hand the partner (wave w ^ 4, the same slab) its two column
+                // tiles of this wave's partial O, and take this wave's from it
+                char *xw = xbuf + (w ^ 4) * 2048 + l * 16;
+                *reinterpret_cast<f32x4_t *>(xw) = O[0][2];
+                *reinterpret_cast<f32x4_t *>(xw + 1024) = O[0][3];
+                wait_vm_lgkm0<63>();
+                wg_barrier();
+                const char *xr = xbuf + w * 2048 + l * 16;
+                O[0][0] += *reinterpret_cast<const f32x4_t *>(xr);
+                O[0][1] += *reinterpret_cast<const f32x4_t *>(xr + 1024);
+            }
             // ---- store O: lane holds row (16*slab + c), columns 16*ct + 4g .. +3
             // (buffer stores from inline asm, outside the compiler's count of
             // outstanding loads; rows past the chunk end are dropped)
