@@ -2,7 +2,16 @@
 (dtype, head dim, block size, dense or packed input with empty sequences,
 forced chunk and sub-chunk lengths, initial/final states or a pool with a
 slot table, the rotary prologue with position offsets), each against the CPU
-oracle.  Sizes stay small enough for the oracle's closed forms."""
+oracle.  Sizes stay small enough for the oracle's closed forms.
+
+With the rotary prologue the reference rotates q and k in float64 and rounds
+the rotated values to the kernel's operand type (bf16 or fp32), then takes
+the closed form on those operands: the bf16 prefill feeds the rotated q and k
+to its products rounded to bf16, and a very short sequence's output can be a
+few dot products that nearly cancel, whose error against the exactly rotated
+values then exceeds the bar relative to that small output (for one stateless
+token about 11% of random draws do) although the kernel computes the rounded
+operands' result to within the rounding of its scores."""
 import numpy as np
 import pytest
 
@@ -50,6 +59,27 @@ def _draw(seed):
     c["base"] = float(r.choice([1e4, 1e7]))
     c["seed"] = seed
     return c
+
+
+def _rotated(qh, kh, c, off, cu):
+    """q and k rotated on their first d/2 dims (float64, oracle.rope) at each
+    token's position, rounded to the kernel's operand type."""
+    import torch
+    d = qh.shape[-1]
+    pos = np.zeros(qh.shape[-2], np.int64)
+    if cu is not None:
+        for s in range(len(cu) - 1):
+            pos[cu[s]:cu[s + 1]] = off[s] + np.arange(cu[s + 1] - cu[s])
+    qr, kr = np.empty_like(qh, dtype=np.float64), np.empty_like(kh, dtype=np.float64)
+    for idx in np.ndindex(qh.shape[:-2]):
+        p = pos if cu is not None else off[idx[0]] + np.arange(qh.shape[-2])
+        qr[idx] = oracle.rope(qh[idx].astype(np.float64), p, d // 2, c["base"])
+        kr[idx] = oracle.rope(kh[idx].astype(np.float64), p, d // 2, c["base"])
+    if c["dt"] == "bf16":
+        rnd = lambda x: torch.tensor(x, dtype=torch.float32).bfloat16().float().numpy().astype(np.float64)
+    else:
+        rnd = lambda x: x.astype(np.float32).astype(np.float64)
+    return rnd(qr), rnd(kr)
 
 
 @pytest.mark.parametrize("seed", range(240))
@@ -102,11 +132,13 @@ def test_random_prefill(dev, seed):
         S0h = None
     qh, kh, vh = host(q), host(k), host(v)
     if c["rope"]:
+        qr, kr = _rotated(qh, kh, c, off, cu if c["packed"] else None)
         if c["packed"]:
-            ref, sref = oracle.causal_linear_attention_rope_varlen(qh, kh, vh, cu, d // 2, c["base"], off, S0h)
+            ref, sref = oracle.causal_linear_attention_varlen_state(qr, kr, vh, cu, S0h)
         else:
-            ref, sref = oracle.causal_linear_attention_rope(qh, kh, vh, d // 2, c["base"], off, S0h)
-        # bf16: the rotated keys enter the products rounded to bf16
+            ref, sref = oracle.causal_linear_attention_state(qr, kr, vh, S0h)
+        # bf16: the rotated keys the kernel sums may differ from the rounded
+        # float64 rotation by one bf16 step (its rotation runs in fp32)
         stol = TOL["bf16"] if c["dt"] == "bf16" else STOL["f32"]
     else:
         if c["packed"]:

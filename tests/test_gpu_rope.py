@@ -128,6 +128,35 @@ def test_rope_large_positions(dev):
     assert oracle.rel_err(o, ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("d,B", [(64, 64), (128, 256)])
+def test_rope_bf16_cancelling_single_token(dev, d, B):
+    """One stateless token whose rotated score q~ . k~ nearly cancels (about
+    1% of the sum of |q~_a k~_a|): o = (q~ . k~) v is then small against the
+    terms of its dot product, and rounding the rotated q and k to bf16 (the
+    operands of the bf16 products) moves it by several percent of itself.  The
+    kernel must give the closed form on the bf16-rounded rotations, to within
+    the bf16 rounding of its score."""
+    import torch
+    import linear_attention_attn_amd as la
+    note(f"rope bf16 cancelling single token d={d} B={B}")
+    base, pos = 1e7, 6737632
+    rng = np.random.default_rng(7 + d)
+    bf = lambda x: torch.tensor(np.asarray(x, np.float32)).bfloat16().float().numpy().astype(np.float64)
+    q = bf(rng.standard_normal(d) / 8)
+    qr = oracle.rope(q[None], [pos], d // 2, base)[0]
+    kr = oracle.rope(rng.standard_normal(d)[None] / 8, [pos], d // 2, base)[0]
+    kr = kr - 0.99 * (qr @ kr) / (qr @ qr) * qr
+    k = bf(oracle.rope(kr[None], [-pos], d // 2, base)[0])      # rotated back to position 0
+    kr = oracle.rope(k[None], [pos], d // 2, base)[0]
+    assert abs(qr @ kr) < 0.05 * np.abs(qr * kr).sum()          # the input really cancels
+    v = bf(rng.standard_normal(d))
+    dev_t = lambda x: torch.tensor(np.asarray(x, np.float32)[None, None, None, :], device=dev).bfloat16()
+    o = host(la.fwd(dev_t(q), dev_t(k), dev_t(v), block_size=B, rope_dims=d // 2, rope_base=base,
+                    pos_offset=_i32([pos], dev)))[0, 0, 0]
+    ref = (bf(qr) @ bf(kr)) * v
+    assert oracle.rel_err(o, ref) <= 2.0 ** -7, (oracle.rel_err(o, ref), qr @ kr)
+
+
 @pytest.mark.parametrize("m", [256, 1000])
 def test_rope_split_and_resume(dev, m):
     """Two pieces, the second continued from the first's state at positions
