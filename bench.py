@@ -559,6 +559,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode workload (one line with its figures; for profiling)")
+    ap.add_argument("--rope-only", action="store_true",
+                    help="only the rotary leg (the MiniMax layer through lightning_attn_fwd_rope, timed "
+                         "alternately with the plain call; one line with its figures; for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--workload", default="minimax_layer",
                     choices=["minimax_layer", "long_1m", "tiny_f32", "minimax_layer_f32", "layer_f32_d64",
@@ -593,6 +596,13 @@ def main():
         print(json.dumps({"decode": {"workload": wd.note, "ms_per_step": dms, "gbs": dgbs,
                                      "hbm_frac": dgbs / PEAK_HBM_GBS, "head_steps_per_s": dtok}}),
               flush=True)
+        return
+    if args.rope_only:
+        w = synth.WORKLOADS["minimax_layer"]
+        rms, pms = bench_prefill_state(w, args.steps, args.warmup, dev, rope=True)
+        print(json.dumps({"rope": {"workload": w.note, "ms_per_step": rms,
+                                   "ms_per_step_plain_same_timing": pms,
+                                   "overhead_vs_plain": rms / pms - 1.0}}), flush=True)
         return
     w = synth.WORKLOADS[args.workload]
     if w.kind == "varlen":
