@@ -562,6 +562,9 @@ def main():
     ap.add_argument("--rope-only", action="store_true",
                     help="only the rotary leg (the MiniMax layer through lightning_attn_fwd_rope, timed "
                          "alternately with the plain call; one line with its figures; for profiling)")
+    ap.add_argument("--state-only", action="store_true",
+                    help="only the state-handoff leg (the MiniMax layer through lightning_attn_fwd_state, "
+                         "timed alternately with the plain call; one line with its figures; for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--workload", default="minimax_layer",
                     choices=["minimax_layer", "long_1m", "tiny_f32", "minimax_layer_f32", "layer_f32_d64",
@@ -596,6 +599,13 @@ def main():
         print(json.dumps({"decode": {"workload": wd.note, "ms_per_step": dms, "gbs": dgbs,
                                      "hbm_frac": dgbs / PEAK_HBM_GBS, "head_steps_per_s": dtok}}),
               flush=True)
+        return
+    if args.state_only:
+        w = synth.WORKLOADS["minimax_layer"]
+        sms, pms = bench_prefill_state(w, args.steps, args.warmup, dev)
+        print(json.dumps({"state_handoff": {"workload": w.note, "ms_per_step": sms,
+                                            "ms_per_step_plain_same_timing": pms,
+                                            "overhead_vs_plain": sms / pms - 1.0}}), flush=True)
         return
     if args.rope_only:
         w = synth.WORKLOADS["minimax_layer"]
