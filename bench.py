@@ -451,7 +451,7 @@ def cpu_baseline(w, target_s, info):
 def cpu_baseline_configs(dev, info):
     """The oracle timed on every workload, beside the GPU figures of the same
     run (a baseline only): the tiny fp32 case (naive and recurrent forms), the
-    MiniMax layer, the packed 16 sequences and the decode workload in full,
+    MiniMax layer, both packed workloads and the decode workload in full,
     and the 1M-token prefill on heads 0 and 63 at full length (two units, so
     two cores) with a labelled extrapolation to all 64 heads.  Inputs are the
     workloads' own (generated on the GPU, copied to the host)."""
@@ -510,20 +510,23 @@ def cpu_baseline_configs(dev, info):
     del q, k, v
     log(json.dumps({"cpu long_1m": out["long_1m"]}))
 
-    # packed 16 sequences in full, in groups of 8 heads (host memory)
-    w = synth.WORKLOADS["varlen16"]
-    lengths = synth.varlen_lengths(w.batch, w.len_seed, w.len_lo, w.len_hi)
-    tot = 0.0
-    T = int(synth.cu_from_lengths(lengths)[-1])
-    for h0 in range(0, w.heads, 8):
-        hs = list(range(h0, min(w.heads, h0 + 8)))
-        q, k, v, cu = synth.varlen_inputs(lengths, w.heads, w.head_dim, w.dtype, w.cid, dev, heads_subset=hs)
-        q, k, v = f32(q), f32(k), f32(v)
-        tot += timed(lambda: oracle.causal_linear_attention_varlen(q, k, v, cu, "recurrent", nthreads=threads))
-        del q, k, v
-    out["varlen16"] = {"sample": f"whole workload ({T} tokens x {w.heads} heads, 8 heads per call)",
-                       "threads": threads, "seconds": tot, "tokens_per_s": T / tot}
-    log(json.dumps({"cpu varlen16": out["varlen16"]}))
+    # the packed workloads in full, in groups of 8 heads (host memory)
+    for name in ("varlen16", "varlen_short"):
+        w = synth.WORKLOADS[name]
+        lengths = synth.varlen_lengths(w.batch, w.len_seed, w.len_lo, w.len_hi)
+        tot = 0.0
+        T = int(synth.cu_from_lengths(lengths)[-1])
+        for h0 in range(0, w.heads, 8):
+            hs = list(range(h0, min(w.heads, h0 + 8)))
+            q, k, v, cu = synth.varlen_inputs(lengths, w.heads, w.head_dim, w.dtype, w.cid, dev,
+                                              heads_subset=hs)
+            q, k, v = f32(q), f32(k), f32(v)
+            tot += timed(lambda: oracle.causal_linear_attention_varlen(q, k, v, cu, "recurrent",
+                                                                       nthreads=threads))
+            del q, k, v
+        out[name] = {"sample": f"whole workload ({T} tokens x {w.heads} heads, 8 heads per call)",
+                     "threads": threads, "seconds": tot, "tokens_per_s": T / tot}
+        log(json.dumps({f"cpu {name}": out[name]}))
 
     # decode: every state, all steps
     w = synth.WORKLOADS["decode256"]
