@@ -1512,10 +1512,10 @@ struct QSplit {
 // with P = mask(Q K^T), then S += K^T V.
 //
 // K and V stream through a 4-stage LDS ring in TJ = 64-token tiles, loaded
-// by buffer loads straight into LDS; tile t + LA (LA = 2) is requested while
-// tile t is used.  Two tiles in flight per CU (64 KiB) already reach the
-// bandwidth that three do with the products left out, and with them the
-// whole kernel is about 1% faster (the fourth stage holds the tile before).
+// by buffer loads straight into LDS; tile t + LA is requested while tile t is
+// used.  The launcher takes LA = 2 (the fourth stage holds the tile before)
+// except for chunks of kLongChunkTokens or more, where LA = 3 (the stage of
+// tile t - 1, released by the barrier that ends it).
 // The four tiles of a ring cycle (a "super-block" of 256 tokens, one
 // or more whole blocks) are separate compile-time copies of the tile body, so
 // a tile's stage, its place in its block and its wait counts are constants.
@@ -2001,6 +2001,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_dma(KParams p) {
 // 256) and d = 128 (blocks of 128), and 23% slower for d = 128, blocks of 64.
 constexpr int fused_waves(int D, int BLK) { return BLK == 64 ? 8 : 16; }
 
+// K/V tiles in flight in the bf16 fused kernel: three for chunks of this many
+// tokens or more, two otherwise.  Alternating in one session on MI355X, three
+// were 4-6% faster at 64 heads x 1M tokens (chunks of 262,144), neutral at
+// chunks of 32,768-65,536 and 0.5-2.7% slower on the MiniMax layer (chunks of
+// 8,192) and on packed sequences of 64-2,047 tokens; outputs bit-identical.
+constexpr int64_t kLongChunkTokens = 131072;
+
 template <typename T, int D, int BLK, bool ROPE>
 static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream_t st, void *const *ev) {
     auto mark = [&](int i) {
@@ -2036,9 +2043,16 @@ static hipError_t launch_typed(const KParams &kp, const FwdPlan &plan, hipStream
         hipLaunchKernelGGL(k_scan_apply<D>, gtiles, dim3(kScanThreads), 0, st, kp, plan.scan_tiles ? 1 : 0);
     }
     mark(3);
-    if constexpr (sizeof(T) == 2)
-        {
+    if constexpr (sizeof(T) == 2) {
         constexpr int NWF = fused_waves(D, BLK);
+        if constexpr (BLK >= 128 && !ROPE) {
+            if (plan.chunk >= kLongChunkTokens) {
+                hipLaunchKernelGGL((k_fused_dma<D, BLK, NWF, 64, 4, 3, ROPE>), gchunks, dim3(NWF * 64), 0, st,
+                                   kp);
+                mark(4);
+                return hipGetLastError();
+            }
+        }
         hipLaunchKernelGGL((k_fused_dma<D, BLK, NWF, 64, 4, 2, ROPE>), gchunks, dim3(NWF * 64), 0, st, kp);
     }
     else if constexpr (D == 64 && !ROPE)

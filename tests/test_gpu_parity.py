@@ -157,6 +157,28 @@ def test_one_hot_boundaries(dev):
             assert np.array_equal(o, expect), (j0, C, S)
 
 
+@pytest.mark.parametrize("d,B", [(128, 256), (64, 128)])
+def test_long_chunks_three_tiles_in_flight(dev, d, B):
+    """Chunks of 131,072 tokens or more run the bf16 fused kernel with three
+    K/V tiles in flight instead of two: dense sequences of two such chunks
+    and a packed mix with one long sequence, against the oracle."""
+    import torch
+    n = 131072 + 9001
+    note(f"long chunks d={d} B={B} n={n}")
+    q, k, v = randn_qkv((1, 2, n, d), "bf16", 4242 + d, dev)
+    with chunk_tokens(131072):
+        o = host(_fwd(q, k, v, B))
+    ref = oracle.causal_linear_attention(host(q), host(k), host(v), "recurrent")
+    assert oracle.rel_err(o, ref) <= TOL["bf16"]
+    lengths = [150001, 5, 0, 70000]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    q, k, v = randn_qkv((2, int(cu[-1]), d), "bf16", 4343 + d, dev)
+    with chunk_tokens(131072):
+        o = host(_fwd(q, k, v, B, torch.from_numpy(cu).to(dev)))
+    ref = oracle.causal_linear_attention_varlen(host(q), host(k), host(v), cu, "recurrent")
+    assert oracle.rel_err(o, ref) <= TOL["bf16"]
+
+
 # ----------------------------------------------------------------- packing
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
