@@ -2006,6 +2006,8 @@ constexpr int fused_waves(int D, int BLK) { return BLK == 64 ? 8 : 16; }
 // were 4-6% faster at 64 heads x 1M tokens (chunks of 262,144), neutral at
 // chunks of 32,768-65,536 and 0.5-2.7% slower on the MiniMax layer (chunks of
 // 8,192) and on packed sequences of 64-2,047 tokens; outputs bit-identical.
+// The rotary instance measured the same with either at 1M tokens (its
+// rotation work is what sets its pace there) and keeps two.
 constexpr int64_t kLongChunkTokens = 131072;
 
 template <typename T, int D, int BLK, bool ROPE>
